@@ -1,0 +1,160 @@
+/*
+ * varq.h - C ABI of the MI355X (gfx950) VAR-Q packed KV-cache library.
+ *
+ * VAR-Q (project page "VAR-Q: Tuning-free KV Cache Quantization for Visual
+ * Autoregressive Image and Video Generation") keeps one scale factor per
+ * feature channel within each generation block (a resolution scale or a
+ * frame), stores 2-8 bit codes packed into INT32 containers, and unpacks and
+ * dequantizes them to BF16 for attention (project page: summary, "Next-block
+ * prediction", "Quantization, bit packing, and retrieval" / Fig. 8). The README
+ * section "Memory-Efficient Runtime" names the compiled operators this library
+ * provides: quantize+pack, unpack+dequant and packed-KV attention, with compact
+ * per-group scales and exact cache preallocation.
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *    frees them and keeps no reference after the call returns.
+ *  - `group_offsets` is a HOST array of G+1 int32 prefix offsets
+ *    0 = o_0 < o_1 < ... < o_G: block g covers tokens [o_g, o_{g+1}).
+ *    G <= VARQ_MAX_GROUPS per call.
+ *  - Strides are in elements. The channel (head_dim) stride is 1 ("BLHc"
+ *    layout of the README's qkv_format: [batch, token, head, channel]).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on that stream and returns; results are ready when the
+ *    stream reaches them.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is launched and a negative varq_status is returned.
+ *    varq_last_error() then describes the failure (per calling thread).
+ *  - Inputs must be finite (NaN/Inf are outside the contract).
+ *
+ * Data layout (this library's reading; the pages fix no layout)
+ *  - bits b in 2..8; qmax = 2^(b-1) - 1; cpw = floor(32/b) codes per word;
+ *    W = ceil(D / cpw) words per (batch, head, token).
+ *  - Packed cache: int32 [B, H, W, L_cap]: plane w of (batch, head) holds word w
+ *    of every token. Field i (bits [i*b, i*b+b)) of word w is the code of channel
+ *    w*cpw + i in b-bit two's complement; unused fields and bits are zero.
+ *  - Scales: fp32 [B, H, G_cap, D], one per (batch, head, block, channel),
+ *    s = fp32(absmax / qmax); never expanded per token.
+ *  - Codes: q = clamp(rint(fp32(x / s)), -qmax, qmax) with IEEE division and
+ *    ties to even; q = 0 when s = 0. Dequantized value: bf16_rne(fp32(q) * s).
+ */
+#ifndef VARQ_H
+#define VARQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum varq_status {
+    VARQ_OK = 0,
+    VARQ_EINVAL = -1,       /* bad size, count, stride, null pointer or group table */
+    VARQ_EBITS = -2,        /* bits outside 2..8 */
+    VARQ_EALIGN = -3,       /* pointer or stride not aligned as documented */
+    VARQ_ECAPACITY = -4,    /* write or read range outside the preallocated cache */
+    VARQ_ELAUNCH = -5,      /* the HIP runtime reported an error */
+    VARQ_EUNSUPPORTED = -6  /* valid request the kernels do not implement (e.g. head_dim) */
+} varq_status;
+
+#define VARQ_MAX_GROUPS 256
+
+/* Codes of `bits` bits per INT32 container: floor(32/bits); 0 if bits is not in 2..8. */
+int varq_codes_per_word(int bits);
+
+/* INT32 words per (batch, head, token) row: ceil(head_dim / floor(32/bits));
+ * 0 if bits is not in 2..8 or head_dim < 1. */
+int varq_words_per_row(int head_dim, int bits);
+
+/*
+ * Exact persistent size of ONE packed tensor (K or V) and of its scales, for
+ * preallocation to the known generation length (README "Memory-Efficient
+ * Runtime": expected_total_seq_len / preallocate_kv_cache):
+ *   *packed_bytes = B*H*W*L_cap*4,  *scale_bytes = B*H*G_cap*head_dim*4.
+ * Either output pointer may be NULL. Pure host arithmetic.
+ */
+int varq_cache_bytes(int B, int H, int head_dim, int64_t L_cap, int64_t G_cap, int bits,
+                     int64_t *packed_bytes, int64_t *scale_bytes);
+
+/*
+ * quantize+pack (project page summary and Fig. 8; README "Memory-Efficient
+ * Runtime"): for every (batch b, head h, block g, channel c) of the input,
+ * a = max |x| over the block's tokens, s = fp32(a/qmax); every element gets the
+ * code q defined above; codes are packed into INT32 words.
+ *
+ *  x            bf16 [B, L_in, H, D] at element strides (sx_b, sx_l, sx_h), channel
+ *               stride 1. Pointer 16-byte aligned; strides multiples of 8.
+ *  group_offsets host int32[G_in+1], block boundaries relative to x (o_{G_in} = L_in).
+ *  packed       int32 [B, H, W, L_cap]; rows [tok_start, tok_start+L_in) of every
+ *               plane are written, nothing else. 16-byte aligned; L_cap % 8 == 0.
+ *  scales       fp32 [B, H, G_cap, D]; slots [group_start, group_start+G_in) are
+ *               written, nothing else. 4-byte aligned.
+ *  D            head_dim: a multiple of 8, 8 <= D <= 256.
+ * Errors: VARQ_EBITS, VARQ_EINVAL, VARQ_EALIGN, VARQ_ECAPACITY
+ * (tok_start+L_in > L_cap or group_start+G_in > G_cap), VARQ_ELAUNCH.
+ * Deterministic: the output does not depend on launch order or timing.
+ */
+int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
+                       int B, int H, int D, int64_t L_in,
+                       const int32_t *group_offsets, int G_in, int bits,
+                       int32_t *packed, int64_t L_cap, int64_t tok_start,
+                       float *scales, int64_t G_cap, int64_t group_start,
+                       void *stream);
+
+/*
+ * Packed-KV attention (project page "Next-block prediction": a block attends to
+ * the cache of all earlier blocks and itself; README: packed-KV load, unpack and
+ * dequant fused into attention). For every (b, h) and query row i:
+ *   O[b,i,h,:] = softmax_j(Q[b,i,h,:] . K^[b,h,j,:] * softmax_scale) V^[b,h,j,:]
+ * over the window j in [0, L_kv) with no mask, where K^, V^ are the dequantized
+ * caches. Logits, softmax and accumulation in fp32; output rounded to bf16.
+ *
+ *  q            bf16 [B, Lq, H, D] at strides (sq_b, sq_l, sq_h); 16-byte aligned,
+ *               strides multiples of 8.
+ *  packed_k/v   int32 [B, H, W, L_cap] written by varq_quantize_pack (16-byte aligned).
+ *  scales_k/v   fp32 [B, H, G_cap, D].
+ *  group_offsets host int32[G+1]: the block boundaries in cache tokens used when
+ *               the cache was written; o_G = L_kv <= L_cap, G <= G_cap.
+ *  D            64 or 128.
+ *  out          bf16 [B, Lq, H, D] at strides (so_b, so_l, so_h); 8-byte aligned,
+ *               strides multiples of 4. Must not overlap q or the cache.
+ * Errors: VARQ_EBITS, VARQ_EINVAL, VARQ_EALIGN, VARQ_ECAPACITY, VARQ_EUNSUPPORTED
+ * (D not 64/128), VARQ_ELAUNCH.
+ */
+int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
+                          int B, int H, int D, int64_t Lq,
+                          const int32_t *packed_k, const float *scales_k,
+                          const int32_t *packed_v, const float *scales_v,
+                          int64_t L_cap, int64_t G_cap, int64_t L_kv,
+                          const int32_t *group_offsets, int G, int bits,
+                          float softmax_scale,
+                          void *out, int64_t so_b, int64_t so_l, int64_t so_h,
+                          void *stream);
+
+/*
+ * unpack+dequant (README "Memory-Efficient Runtime"; project page Fig. 8): the
+ * dense bf16 view of tokens [0, L) of a packed cache,
+ *   out[b, h, t, c] = bf16_rne(fp32(q[b,h,t,c]) * s[b,h,g(t),c]),
+ * g(t) the block holding t. Used by the unfused attention path and by tests.
+ *
+ *  packed, scales as above; group_offsets host int32[G+1] with o_G = L <= L_cap.
+ *  out          bf16 [B, H, L, D], contiguous, 16-byte aligned.
+ *  D            a multiple of 8, 8 <= D <= 256.
+ * Errors: as varq_quantize_pack.
+ */
+int varq_unpack_dequant(const int32_t *packed, const float *scales,
+                        int B, int H, int D, int64_t L_cap, int64_t G_cap, int64_t L,
+                        const int32_t *group_offsets, int G, int bits,
+                        void *out, void *stream);
+
+/* Text of the last error reported to the calling thread ("" if none). */
+const char *varq_last_error(void);
+
+/* Library version string. */
+const char *varq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VARQ_H */

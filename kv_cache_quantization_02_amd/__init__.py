@@ -1,0 +1,18 @@
+"""MI355X (gfx950) implementation of VAR-Q's packed KV-cache hot path.
+
+The compute lives in libvarq.so (C ABI in include/varq.h): quantize+pack,
+unpack+dequant and packed-KV attention as hand-written HIP kernels. The module
+`varq` is a thin ctypes binding over it.
+"""
+
+from . import varq  # noqa: F401
+from .varq import (  # noqa: F401
+    VarqError,
+    alloc_cache,
+    cache_bytes,
+    codes_per_word,
+    packed_attention,
+    quantize_pack,
+    unpack_dequant,
+    words_per_row,
+)

@@ -1,0 +1,256 @@
+// varq_api.cpp - C ABI of the VAR-Q packed KV-cache library: argument
+// validation, work decomposition and launches on the caller's stream.
+// Nothing here computes on the host beyond sizes and launch tables; every step
+// of quantization, packing and attention runs in the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/varq.h"
+#include "varq_device.h"
+
+namespace varq {
+hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, hipStream_t st);
+hipError_t launch_unpack_dequant(const UnpackArgs &a, int bits, hipStream_t st);
+hipError_t launch_packed_attention(const AttnArgs &a, int D, int bits, hipStream_t st);
+int attention_q_tile();
+}  // namespace varq
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return VARQ_OK;
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int check_bits(int bits) {
+    if (bits < 2 || bits > 8) return fail(VARQ_EBITS, "bits must be in 2..8 (got %d)", bits);
+    return VARQ_OK;
+}
+
+// group_offsets: host int32[G+1], 0 = o_0 < ... < o_G = L.
+int check_offsets(const int32_t *off, int G, int64_t L, const char *what) {
+    if (G < 1 || G > VARQ_MAX_GROUPS)
+        return fail(VARQ_EINVAL, "%s: number of blocks G=%d outside 1..%d", what, G, VARQ_MAX_GROUPS);
+    if (off == nullptr) return fail(VARQ_EINVAL, "%s: group_offsets is NULL", what);
+    if (off[0] != 0) return fail(VARQ_EINVAL, "%s: group_offsets[0] must be 0 (got %d)", what, off[0]);
+    for (int g = 0; g < G; ++g)
+        if (off[g + 1] <= off[g])
+            return fail(VARQ_EINVAL, "%s: group_offsets must strictly increase (o[%d]=%d, o[%d]=%d)",
+                        what, g, off[g], g + 1, off[g + 1]);
+    if ((int64_t)off[G] != L)
+        return fail(VARQ_EINVAL, "%s: group_offsets[G] = %d must equal the token count %lld", what,
+                    off[G], (long long)L);
+    return VARQ_OK;
+}
+
+int launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(VARQ_ELAUNCH, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+    return ok();
+}
+
+int words_per_row(int D, int bits) {
+    const int cpw = 32 / bits;
+    return (D + cpw - 1) / cpw;
+}
+
+int gcd(int x, int y) {
+    while (y) {
+        const int t = x % y;
+        x = y;
+        y = t;
+    }
+    return x;
+}
+
+}  // namespace
+
+extern "C" {
+
+int varq_codes_per_word(int bits) { return (bits >= 2 && bits <= 8) ? 32 / bits : 0; }
+
+int varq_words_per_row(int head_dim, int bits) {
+    if (bits < 2 || bits > 8 || head_dim < 1) return 0;
+    return words_per_row(head_dim, bits);
+}
+
+int varq_cache_bytes(int B, int H, int head_dim, int64_t L_cap, int64_t G_cap, int bits,
+                     int64_t *packed_bytes, int64_t *scale_bytes) {
+    if (int r = check_bits(bits)) return r;
+    if (B < 1 || H < 1 || head_dim < 1 || L_cap < 0 || G_cap < 0)
+        return fail(VARQ_EINVAL, "cache_bytes: sizes must be positive (B=%d H=%d D=%d L_cap=%lld G_cap=%lld)",
+                    B, H, head_dim, (long long)L_cap, (long long)G_cap);
+    const int64_t W = words_per_row(head_dim, bits);
+    if (packed_bytes) *packed_bytes = (int64_t)B * H * W * L_cap * 4;
+    if (scale_bytes) *scale_bytes = (int64_t)B * H * G_cap * head_dim * 4;
+    return ok();
+}
+
+int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
+                       int B, int H, int D, int64_t L_in,
+                       const int32_t *group_offsets, int G_in, int bits,
+                       int32_t *packed, int64_t L_cap, int64_t tok_start,
+                       float *scales, int64_t G_cap, int64_t group_start,
+                       void *stream) {
+    if (int r = check_bits(bits)) return r;
+    if (B < 1 || H < 1) return fail(VARQ_EINVAL, "quantize_pack: B=%d H=%d must be >= 1", B, H);
+    if (D < 8 || D > 256 || D % 8 != 0)
+        return fail(VARQ_EINVAL, "quantize_pack: head_dim %d must be a multiple of 8 in 8..256", D);
+    if (L_in < 0) return fail(VARQ_EINVAL, "quantize_pack: L_in=%lld < 0", (long long)L_in);
+    if (L_in == 0 && G_in == 0) return ok();                       // nothing to write
+    if (int r = check_offsets(group_offsets, G_in, L_in, "quantize_pack")) return r;
+    if (!x || !packed || !scales) return fail(VARQ_EINVAL, "quantize_pack: NULL tensor pointer");
+    if (!aligned(x, 16) || sx_b % 8 || sx_l % 8 || sx_h % 8)
+        return fail(VARQ_EALIGN, "quantize_pack: x must be 16-byte aligned with strides that are multiples of 8");
+    if (!aligned(packed, 16) || L_cap % 8)
+        return fail(VARQ_EALIGN, "quantize_pack: packed must be 16-byte aligned and L_cap a multiple of 8");
+    if (!aligned(scales, 4)) return fail(VARQ_EALIGN, "quantize_pack: scales must be 4-byte aligned");
+    if (tok_start < 0 || group_start < 0 || tok_start + L_in > L_cap || group_start + G_in > G_cap)
+        return fail(VARQ_ECAPACITY,
+                    "quantize_pack: rows [%lld, %lld) / blocks [%lld, %lld) exceed the cache (L_cap=%lld, G_cap=%lld)",
+                    (long long)tok_start, (long long)(tok_start + L_in), (long long)group_start,
+                    (long long)(group_start + G_in), (long long)L_cap, (long long)G_cap);
+
+    varq::QuantPackArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = static_cast<const uint16_t *>(x);
+    a.sx_b = sx_b; a.sx_l = sx_l; a.sx_h = sx_h;
+    a.packed = reinterpret_cast<uint32_t *>(packed);
+    a.scales = scales;
+    a.L_cap = L_cap; a.tok_start = tok_start; a.G_cap = G_cap; a.group_start = group_start;
+    a.B = B; a.H = H; a.D = D; a.G = G_in;
+    const int cpw = 32 / bits;
+    a.W = words_per_row(D, bits);
+    // Slices of whole words whose first channel is a multiple of 8 (16-byte
+    // loads); sized so that one unit stays near 16K elements.
+    const int align_w = 8 / gcd(8, cpw);
+    const int64_t target = 16384;
+    int64_t units = 0;
+    for (int g = 0; g < G_in; ++g) {
+        a.off[g] = group_offsets[g];
+        const int64_t n = group_offsets[g + 1] - group_offsets[g];
+        int64_t sw = target / (n * cpw);
+        sw = (sw / align_w) * align_w;
+        if (sw < align_w) sw = align_w;
+        if (sw >= a.W) sw = a.W;
+        a.slice_words[g] = (uint8_t)sw;
+        a.unit_start[g] = (int32_t)units;
+        units += (int64_t)B * H * ((a.W + sw - 1) / sw);
+    }
+    a.off[G_in] = group_offsets[G_in];
+    a.unit_start[G_in] = (int32_t)units;
+    if (units >= (1LL << 31) - 8) return fail(VARQ_EINVAL, "quantize_pack: too many work units");
+    a.n_units = (int)units;
+    return launch_status(varq::launch_quant_pack(a, bits, static_cast<hipStream_t>(stream)), "quantize_pack");
+}
+
+int varq_unpack_dequant(const int32_t *packed, const float *scales,
+                        int B, int H, int D, int64_t L_cap, int64_t G_cap, int64_t L,
+                        const int32_t *group_offsets, int G, int bits,
+                        void *out, void *stream) {
+    if (int r = check_bits(bits)) return r;
+    if (B < 1 || H < 1) return fail(VARQ_EINVAL, "unpack_dequant: B=%d H=%d must be >= 1", B, H);
+    if (D < 8 || D > 256 || D % 8 != 0)
+        return fail(VARQ_EINVAL, "unpack_dequant: head_dim %d must be a multiple of 8 in 8..256", D);
+    if (L < 0) return fail(VARQ_EINVAL, "unpack_dequant: L=%lld < 0", (long long)L);
+    if (L == 0 && G == 0) return ok();
+    if (int r = check_offsets(group_offsets, G, L, "unpack_dequant")) return r;
+    if (!packed || !scales || !out) return fail(VARQ_EINVAL, "unpack_dequant: NULL tensor pointer");
+    if (!aligned(packed, 16) || L_cap % 8)
+        return fail(VARQ_EALIGN, "unpack_dequant: packed must be 16-byte aligned and L_cap a multiple of 8");
+    if (!aligned(out, 16)) return fail(VARQ_EALIGN, "unpack_dequant: out must be 16-byte aligned");
+    if (!aligned(scales, 4)) return fail(VARQ_EALIGN, "unpack_dequant: scales must be 4-byte aligned");
+    if (L > L_cap || G > G_cap)
+        return fail(VARQ_ECAPACITY, "unpack_dequant: L=%lld / G=%d exceed L_cap=%lld / G_cap=%lld",
+                    (long long)L, G, (long long)L_cap, (long long)G_cap);
+    const int64_t items = (int64_t)B * H * L * (D / 8);
+    if (items / 256 >= (1LL << 31)) return fail(VARQ_EINVAL, "unpack_dequant: tensor too large");
+
+    varq::UnpackArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.packed = reinterpret_cast<const uint32_t *>(packed);
+    a.scales = scales;
+    a.out = static_cast<uint16_t *>(out);
+    a.L_cap = L_cap; a.G_cap = G_cap; a.L = L;
+    a.B = B; a.H = H; a.D = D; a.W = words_per_row(D, bits); a.G = G;
+    for (int g = 0; g <= G; ++g) a.off[g] = group_offsets[g];
+    return launch_status(varq::launch_unpack_dequant(a, bits, static_cast<hipStream_t>(stream)), "unpack_dequant");
+}
+
+int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
+                          int B, int H, int D, int64_t Lq,
+                          const int32_t *packed_k, const float *scales_k,
+                          const int32_t *packed_v, const float *scales_v,
+                          int64_t L_cap, int64_t G_cap, int64_t L_kv,
+                          const int32_t *group_offsets, int G, int bits,
+                          float softmax_scale,
+                          void *out, int64_t so_b, int64_t so_l, int64_t so_h,
+                          void *stream) {
+    if (int r = check_bits(bits)) return r;
+    if (B < 1 || H < 1) return fail(VARQ_EINVAL, "packed_attention: B=%d H=%d must be >= 1", B, H);
+    if (D != 64 && D != 128)
+        return fail(VARQ_EUNSUPPORTED, "packed_attention: head_dim %d not implemented (64 or 128)", D);
+    if (Lq < 0) return fail(VARQ_EINVAL, "packed_attention: Lq=%lld < 0", (long long)Lq);
+    if (Lq == 0) return ok();
+    if (L_kv < 1) return fail(VARQ_EINVAL, "packed_attention: the window is empty (L_kv=%lld)", (long long)L_kv);
+    if (int r = check_offsets(group_offsets, G, L_kv, "packed_attention")) return r;
+    if (!q || !packed_k || !scales_k || !packed_v || !scales_v || !out)
+        return fail(VARQ_EINVAL, "packed_attention: NULL tensor pointer");
+    if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f)
+        return fail(VARQ_EINVAL, "packed_attention: softmax_scale must be finite and > 0");
+    if (!aligned(q, 16) || sq_b % 8 || sq_l % 8 || sq_h % 8)
+        return fail(VARQ_EALIGN, "packed_attention: q must be 16-byte aligned with strides that are multiples of 8");
+    if (!aligned(out, 8) || so_b % 4 || so_l % 4 || so_h % 4)
+        return fail(VARQ_EALIGN, "packed_attention: out must be 8-byte aligned with strides that are multiples of 4");
+    if (!aligned(packed_k, 16) || !aligned(packed_v, 16) || L_cap % 8)
+        return fail(VARQ_EALIGN, "packed_attention: packed caches must be 16-byte aligned and L_cap a multiple of 8");
+    if (!aligned(scales_k, 4) || !aligned(scales_v, 4))
+        return fail(VARQ_EALIGN, "packed_attention: scales must be 4-byte aligned");
+    if (L_kv > L_cap || G > G_cap)
+        return fail(VARQ_ECAPACITY, "packed_attention: L_kv=%lld / G=%d exceed L_cap=%lld / G_cap=%lld",
+                    (long long)L_kv, G, (long long)L_cap, (long long)G_cap);
+    const int qtile = varq::attention_q_tile();
+    const int64_t n_qtiles = (Lq + qtile - 1) / qtile;
+    if (n_qtiles * B * H >= (1LL << 31) - 8) return fail(VARQ_EINVAL, "packed_attention: grid too large");
+
+    varq::AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = static_cast<const uint16_t *>(q);
+    a.sq_b = sq_b; a.sq_l = sq_l; a.sq_h = sq_h;
+    a.pk = reinterpret_cast<const uint32_t *>(packed_k);
+    a.pv = reinterpret_cast<const uint32_t *>(packed_v);
+    a.sk = scales_k; a.sv = scales_v;
+    a.out = static_cast<uint16_t *>(out);
+    a.so_b = so_b; a.so_l = so_l; a.so_h = so_h;
+    a.L_cap = L_cap; a.G_cap = G_cap; a.L_kv = L_kv; a.Lq = Lq;
+    a.B = B; a.H = H; a.W = words_per_row(D, bits); a.G = G;
+    a.n_qtiles = (int)n_qtiles;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    for (int g = 0; g <= G; ++g) a.off[g] = group_offsets[g];
+    return launch_status(varq::launch_packed_attention(a, D, bits, static_cast<hipStream_t>(stream)),
+                         "packed_attention");
+}
+
+const char *varq_last_error(void) { return g_last_error.c_str(); }
+
+const char *varq_version(void) { return "varq-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

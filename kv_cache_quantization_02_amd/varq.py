@@ -1,0 +1,206 @@
+"""Thin ctypes binding of libvarq.so (include/varq.h).
+
+Each function marshals torch tensors into the C ABI's pointers, strides and
+stream and calls the entry point of the same name (without the ``varq_``
+prefix). All computation happens in the gfx950 kernels; if the library is not
+built, every call raises. PyTorch supplies device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvarq.so")
+
+VARQ_OK = 0
+STATUS_NAMES = {0: "VARQ_OK", -1: "VARQ_EINVAL", -2: "VARQ_EBITS", -3: "VARQ_EALIGN",
+                -4: "VARQ_ECAPACITY", -5: "VARQ_ELAUNCH", -6: "VARQ_EUNSUPPORTED"}
+MAX_GROUPS = 256
+
+_lib = None
+
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+_SIGNATURES = {
+    "varq_codes_per_word": (_i32, [_i32]),
+    "varq_words_per_row": (_i32, [_i32, _i32]),
+    "varq_cache_bytes": (_i32, [_i32, _i32, _i32, _i64, _i64, _i32, _i64p, _i64p]),
+    "varq_quantize_pack": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i32p, _i32, _i32,
+                                  _vp, _i64, _i64, _vp, _i64, _i64, _vp]),
+    "varq_packed_attention": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64,
+                                     _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32p, _i32, _i32,
+                                     _f32, _vp, _i64, _i64, _i64, _vp]),
+    "varq_unpack_dequant": (_i32, [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32p, _i32, _i32,
+                                   _vp, _vp]),
+    "varq_last_error": (ctypes.c_char_p, []),
+    "varq_version": (ctypes.c_char_p, []),
+}
+
+
+class VarqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded libvarq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status):
+    if status != VARQ_OK:
+        raise VarqError(status, lib().varq_last_error().decode())
+
+
+def _offsets(group_offsets):
+    off = [int(o) for o in group_offsets]
+    arr = (ctypes.c_int32 * len(off))(*off)
+    return arr, len(off) - 1
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA {dtype} tensor")
+
+
+def last_error() -> str:
+    return lib().varq_last_error().decode()
+
+
+def version() -> str:
+    return lib().varq_version().decode()
+
+
+def codes_per_word(bits: int) -> int:
+    return lib().varq_codes_per_word(bits)
+
+
+def words_per_row(head_dim: int, bits: int) -> int:
+    return lib().varq_words_per_row(head_dim, bits)
+
+
+def cache_bytes(B, H, head_dim, L_cap, G_cap, bits):
+    """(packed_bytes, scale_bytes) of one packed tensor and its scales."""
+    p, s = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().varq_cache_bytes(B, H, head_dim, L_cap, G_cap, bits, ctypes.byref(p), ctypes.byref(s)))
+    return p.value, s.value
+
+
+def round_capacity(L):
+    """Token capacity accepted by the library: L rounded up to a multiple of 8."""
+    return (int(L) + 7) // 8 * 8
+
+
+def alloc_cache(B, H, head_dim, L_cap, G_cap, bits, device="cuda"):
+    """Preallocate one packed tensor [B, H, W, L_cap] (int32) and its scales
+    [B, H, G_cap, D] (fp32) with the exact sizes of cache_bytes()."""
+    L_cap = round_capacity(L_cap)
+    pb, sb = cache_bytes(B, H, head_dim, L_cap, G_cap, bits)
+    W = words_per_row(head_dim, bits)
+    packed = torch.zeros(B, H, W, L_cap, dtype=torch.int32, device=device)
+    scales = torch.zeros(B, H, G_cap, head_dim, dtype=torch.float32, device=device)
+    assert packed.numel() * 4 == pb and scales.numel() * 4 == sb
+    return packed, scales
+
+
+def quantize_pack(x, group_offsets, bits, packed, scales, tok_start=0, group_start=0, stream=None):
+    """x bf16 [B, L_in, H, D] (channel stride 1) -> rows [tok_start, tok_start+L_in)
+    of `packed` [B, H, W, L_cap] and slots [group_start, group_start+G_in) of
+    `scales` [B, H, G_cap, D]."""
+    _need(x, torch.bfloat16, "x")
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float32, "scales")
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("x must be [B, L, H, D] with channel stride 1")
+    if not packed.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("packed and scales must be contiguous")
+    B, L, H, D = x.shape
+    off, G = _offsets(group_offsets)
+    _check(lib().varq_quantize_pack(
+        x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, H, D, L, off, G, bits,
+        packed.data_ptr(), packed.shape[3], tok_start, scales.data_ptr(), scales.shape[2],
+        group_start, _stream(stream, x.device)))
+    return packed, scales
+
+
+def packed_attention(q, packed_k, scales_k, packed_v, scales_v, group_offsets, bits,
+                     softmax_scale=None, out=None, stream=None):
+    """q bf16 [B, Lq, H, D] attends to cache tokens [0, group_offsets[-1]) ->
+    out bf16 [B, Lq, H, D]."""
+    _need(q, torch.bfloat16, "q")
+    for t, n in ((packed_k, "packed_k"), (packed_v, "packed_v")):
+        _need(t, torch.int32, n)
+    for t, n in ((scales_k, "scales_k"), (scales_v, "scales_v")):
+        _need(t, torch.float32, n)
+    if q.dim() != 4 or q.stride(3) != 1:
+        raise ValueError("q must be [B, Lq, H, D] with channel stride 1")
+    for t in (packed_k, packed_v, scales_k, scales_v):
+        if not t.is_contiguous():
+            raise ValueError("packed caches and scales must be contiguous")
+    if packed_k.shape != packed_v.shape or scales_k.shape != scales_v.shape:
+        raise ValueError("K and V caches must have the same geometry")
+    B, Lq, H, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    softmax_scale = float(torch.tensor(softmax_scale, dtype=torch.float32))
+    if out is None:
+        out = torch.empty(B, Lq, H, D, dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out")
+    if out.stride(3) != 1:
+        raise ValueError("out must have channel stride 1")
+    off, G = _offsets(group_offsets)
+    L_kv = int(group_offsets[-1])
+    _check(lib().varq_packed_attention(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), B, H, D, Lq,
+        packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
+        packed_k.shape[3], scales_k.shape[2], L_kv, off, G, bits, softmax_scale,
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2), _stream(stream, q.device)))
+    return out
+
+
+def unpack_dequant(packed, scales, group_offsets, bits, out=None, stream=None):
+    """Dense bf16 [B, H, L, D] view of cache tokens [0, group_offsets[-1])."""
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float32, "scales")
+    if not packed.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("packed and scales must be contiguous")
+    B, H, _, L_cap = packed.shape
+    D = scales.shape[3]
+    L = int(group_offsets[-1])
+    if out is None:
+        out = torch.empty(B, H, L, D, dtype=torch.bfloat16, device=packed.device)
+    _need(out, torch.bfloat16, "out")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    off, G = _offsets(group_offsets)
+    _check(lib().varq_unpack_dequant(
+        packed.data_ptr(), scales.data_ptr(), B, H, D, L_cap, scales.shape[2], L, off, G, bits,
+        out.data_ptr(), _stream(stream, packed.device)))
+    return out
