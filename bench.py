@@ -46,7 +46,22 @@ def parse():
     p.add_argument("--bits", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="only run 5 plain device-to-device copies of BYTES bytes (counter calibration)")
     return p.parse_args()
+
+
+def copy_probe(nbytes):
+    """Five plain device copies of a known size: the reference that scales the
+    HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the kernels."""
+    import torch
+    x = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "copies": 5}), flush=True)
 
 
 # ---------------------------------------------------------------- algorithmic work
@@ -153,6 +168,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU sharding is "
               "described in the design notes but not built.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     import torch
 
     from kv_cache_quantization_02_amd import varq
