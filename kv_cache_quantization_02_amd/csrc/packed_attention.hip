@@ -5,265 +5,423 @@
 // README "Deployment Results" / "Memory-Efficient Runtime": loading the packed
 // cache, unpacking and dequantizing are fused into attention.
 //
-// Work-group = 4 waves x 32 queries of one (batch, head). Per 64-token tile:
-//  1. all 256 threads read packed words straight from HBM (each thread: one
-//     word plane x 8 consecutive tokens = 32 bytes), dequantize them exactly to
-//     bf16_rne(q * s[block(t), c]) and write K row-major (token x channel) and V
-//     transposed (channel x token) into LDS;
-//  2. each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (lanes hold
-//     one query each, so the softmax row statistics are lane-local), runs an
-//     online fp32 softmax in base 2, and accumulates O^T = V^T P^T with P kept in
-//     registers: the accumulator layout of S^T is the B-operand layout of the PV
-//     product up to a fixed permutation of the 16 tokens of a k-step, which the
-//     V^T operand reads follow.
+// Work-group = 4 waves x 64 queries of one (batch, head); KV tiles of 64 tokens,
+// software pipelined with one LDS barrier per tile:
+//  * packed words of tile j+2 are fetched from HBM into registers (each thread
+//    owns one (word plane, 8 consecutive tokens) item = one 32-byte load);
+//  * tile j+1 is dequantized exactly, bf16_rne(q * s[block(t), c]), from those
+//    registers into the free half of a double-buffered LDS - K row-major
+//    (token x channel), V transposed (channel x token) - placed right after the
+//    first matrix-core batch of tile j so that it overlaps it;
+//  * tile j is consumed by each wave: S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+//    (lanes own one query each, so softmax statistics are lane-local), an online
+//    base-2 softmax in fp32 that rescales the accumulators only when some lane's
+//    running maximum grows by more than 2^8, and O^T += V^T P^T with P taken
+//    straight from the S^T accumulators (their layout is the B-operand layout of
+//    the PV product up to a fixed permutation of each 16-token k-step, which the
+//    V^T layout follows). Every K/V operand read from LDS feeds the wave's two
+//    32-query blocks. Row sums use v_dot2 on the bf16 P actually multiplied.
+// Only the last tile masks tokens past the window; only tiles that contain a
+// block boundary take the per-token scale path.
 #include "varq_device.h"
 
 namespace varq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int AT_THREADS = 256;
-constexpr int AT_NT = 64;       // KV tokens per tile
-constexpr int AT_QT = 128;      // queries per work-group (4 waves x 32)
+constexpr int AT_NT = 64;        // KV tokens per tile
+constexpr float AT_RESCALE_SLACK = 8.0f;   // log2 units: p <= 2^8 between rescales
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int BITS, int D>
-__global__ __launch_bounds__(AT_THREADS) void packed_attention_v1(const AttnArgs a) {
-    constexpr int CPW = 32 / BITS;
-    constexpr int W = (D + CPW - 1) / CPW;
+__device__ inline bf16x2 ones_bf16x2() {
+    return __builtin_bit_cast(bf16x2, 0x3F803F80u);
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    floatx2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+template <int BITS>
+__device__ inline float field_f32(uint32_t word, int i) {
     constexpr int SHIFT = 32 - BITS;
-    constexpr int KP = D + 8;            // K row pitch (bf16)
-    constexpr int VP = AT_NT + 8;        // V^T row pitch (bf16)
+    return (float)((int32_t)(word << (SHIFT - i * BITS)) >> SHIFT);
+}
+
+// o *= alpha on an accumulator tile that lives in AGPRs: read, scale, write
+// back in place, so the accumulators never have to move to VGPRs.
+__device__ inline void scale_acc16(floatx16 &o, float alpha) {
+    float tmp;
+#define VARQ_SCALE_ONE(R)                                                              \
+    asm volatile("v_accvgpr_read_b32 %0, %1\n\tv_mul_f32 %0, %0, %2\n\tv_accvgpr_write_b32 %1, %0" \
+                 : "=&v"(tmp), "+a"(o[R]) : "v"(alpha));
+    VARQ_SCALE_ONE(0) VARQ_SCALE_ONE(1) VARQ_SCALE_ONE(2) VARQ_SCALE_ONE(3)
+    VARQ_SCALE_ONE(4) VARQ_SCALE_ONE(5) VARQ_SCALE_ONE(6) VARQ_SCALE_ONE(7)
+    VARQ_SCALE_ONE(8) VARQ_SCALE_ONE(9) VARQ_SCALE_ONE(10) VARQ_SCALE_ONE(11)
+    VARQ_SCALE_ONE(12) VARQ_SCALE_ONE(13) VARQ_SCALE_ONE(14) VARQ_SCALE_ONE(15)
+#undef VARQ_SCALE_ONE
+}
+
+template <int BITS, int D, int QB, int NW>
+struct AttnTile {
+    static constexpr int CPW = 32 / BITS;
+    static constexpr int W = (D + CPW - 1) / CPW;
+    static constexpr int KP = D + 8;          // K row pitch (bf16)
+    static constexpr int VP = AT_NT + 8;      // V^T row pitch (bf16)
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int QW = 32 * QB;        // queries per wave
+    static constexpr int QT = NW * QW;        // queries per work-group
+    static constexpr int NITEMS = 32 * W;     // 16W K items then 16W V items (4 tokens each)
+    static constexpr int IPT = (NITEMS + THREADS - 1) / THREADS;
+};
+
+// V^T tile in LDS: row = channel; inside each 16-token group the four 4-token
+// quarters are stored in the order 0, 2, 1, 3 so that the eight tokens one PV
+// operand lane needs (quarters hf and hf + 2) are contiguous.
+__device__ inline int v_pos(int tok) {
+    const int q = (tok >> 2) & 3;
+    return (tok & ~15) + 4 * (((q & 1) << 1) | (q >> 1)) + (tok & 3);
+}
+
+template <int BITS, int D, int QB, int NW>
+__global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a) {
+    using T = AttnTile<BITS, D, QB, NW>;
+    constexpr int CPW = T::CPW, W = T::W, KP = T::KP, VP = T::VP;
+    constexpr int THREADS = T::THREADS, QW = T::QW, QT = T::QT;
+    constexpr int NITEMS = T::NITEMS, IPT = T::IPT;
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
+    constexpr int KBUF = AT_NT * KP, VBUF = D * VP;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[AT_NT * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
     __shared__ int32_t off[VARQ_MAX_GROUPS_DEV + 1];
 
-    const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H;
-    const int64_t lid = xcd_logical_id(blockIdx.x, n_blocks);
+    const int n_blocks = a.n_qtiles * a.B * a.H;
+    const int lid = (int)xcd_logical_id(blockIdx.x, n_blocks);
     if (lid < 0) return;
-    const int qt = (int)(lid % a.n_qtiles);
-    const int64_t bh = lid / a.n_qtiles;
-    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const int qt = lid % a.n_qtiles;
+    const int bh = lid / a.n_qtiles;
+    const int b = bh / a.H, h = bh % a.H;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 31, hf = lane >> 5;
 
-    for (int i = tid; i <= a.G; i += AT_THREADS) off[i] = a.off[i];
+    for (int i = tid; i <= a.G; i += THREADS) off[i] = a.off[i];
 
-    // Q^T operand: lane = query (lr), slots (hf, j) = channel 16*ks + 8*hf + j
-    const int64_t qi = (int64_t)qt * AT_QT + wave * 32 + lr;
-    const bool qvalid = qi < a.Lq;
-    bf16x8 qop[KSTEPS];
-    {
-        const uint16_t *qrow = a.q + (int64_t)b * a.sq_b + qi * a.sq_l + (int64_t)h * a.sq_h + 8 * hf;
+    // Q^T operands: lane = query, slots (hf, j) = channel 16*ks + 8*hf + j
+    const int q_base = qt * QT + wave * QW + lr;
+    bf16x8 qop[QB][KSTEPS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qi = q_base + 32 * qb;
+        const uint16_t *qrow = a.q + (int64_t)b * a.sq_b + (int64_t)qi * a.sq_l + (int64_t)h * a.sq_h + 8 * hf;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (qvalid) v = *reinterpret_cast<const uint4 *>(qrow + 16 * ks);
-            qop[ks] = as_bf16x8(v);
+            if (qi < a.Lq) v = *reinterpret_cast<const uint4 *>(qrow + 16 * ks);
+            qop[qb][ks] = as_bf16x8(v);
         }
     }
 
-    floatx16 o[DBLK];
-#pragma unroll
-    for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
+    // Retire the Q loads here. Otherwise the wait-count analysis sees them
+    // pending at the loop header and waits for every outstanding load (the
+    // KV prefetch included) before the first matrix-core op of each tile.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-    const uint32_t *pk = a.pk + bh * W * a.L_cap;
-    const uint32_t *pv = a.pv + bh * W * a.L_cap;
-    const float *sk = a.sk + bh * a.G_cap * D;
-    const float *sv = a.sv + bh * a.G_cap * D;
-    int g_tile = 0;
-    __syncthreads();
-
-    for (int64_t n0 = 0; n0 < a.L_kv; n0 += AT_NT) {
-        g_tile = group_of(off, g_tile, n0);
-        __syncthreads();   // previous tile's LDS reads are done
-        // ---- 1. load + unpack + dequant into LDS
-        for (int it = tid; it < 16 * W; it += AT_THREADS) {
-            const bool isV = it >= 8 * W;
-            const int j = isV ? it - 8 * W : it;
-            const int w = j >> 3, tg = j & 7;
-            const int64_t t = n0 + 8 * tg;
-            const uint32_t *plane = (isV ? pv : pk) + (int64_t)w * a.L_cap;
-            uint32_t wd[8];
-            if (t + 8 <= a.L_kv) {
-                const uint4 v0 = *reinterpret_cast<const uint4 *>(plane + t);
-                const uint4 v1 = *reinterpret_cast<const uint4 *>(plane + t + 4);
-                wd[0] = v0.x; wd[1] = v0.y; wd[2] = v0.z; wd[3] = v0.w;
-                wd[4] = v1.x; wd[5] = v1.y; wd[6] = v1.z; wd[7] = v1.w;
-            } else {
+    floatx16 o[QB][DBLK];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) wd[k] = (t + k < a.L_kv) ? plane[t + k] : 0u;
-            }
-            const int cbase = w * CPW;
-            const int ncw = min(CPW, D - cbase);
-            const float *srow_base = isV ? sv : sk;
-            int g = group_of(off, g_tile, t < a.L_kv ? t : a.L_kv - 1);
-            float sc[CPW];
-#pragma unroll
-            for (int i = 0; i < CPW; ++i) sc[i] = (i < ncw) ? srow_base[(int64_t)g * D + cbase + i] : 0.0f;
-            uint16_t vals[8][CPW];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int64_t tk = t + k;
-                if (tk < a.L_kv && off[g + 1] <= tk) {
-                    g = group_of(off, g, tk);
-#pragma unroll
-                    for (int i = 0; i < CPW; ++i)
-                        sc[i] = (i < ncw) ? srow_base[(int64_t)g * D + cbase + i] : 0.0f;
-                }
-#pragma unroll
-                for (int i = 0; i < CPW; ++i) {
-                    const int32_t qv = (int32_t)(wd[k] << (SHIFT - i * BITS)) >> SHIFT;
-                    vals[k][i] = (uint16_t)dequant_bits(qv, sc[i]);
-                }
-            }
-            if (!isV) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    uint16_t *dst = Ks + (8 * tg + k) * KP + cbase;
-                    if constexpr ((CPW * 2) % 16 == 0) {
-#pragma unroll
-                        for (int i = 0; i < CPW; i += 8) {
-                            uint4 v;
-                            v.x = vals[k][i] | ((uint32_t)vals[k][i + 1] << 16);
-                            v.y = vals[k][i + 2] | ((uint32_t)vals[k][i + 3] << 16);
-                            v.z = vals[k][i + 4] | ((uint32_t)vals[k][i + 5] << 16);
-                            v.w = vals[k][i + 6] | ((uint32_t)vals[k][i + 7] << 16);
-                            *reinterpret_cast<uint4 *>(dst + i) = v;
-                        }
-                    } else if constexpr ((CPW * 2) % 8 == 0) {
-#pragma unroll
-                        for (int i = 0; i < CPW; i += 4) {
-                            uint2 v;
-                            v.x = vals[k][i] | ((uint32_t)vals[k][i + 1] << 16);
-                            v.y = vals[k][i + 2] | ((uint32_t)vals[k][i + 3] << 16);
-                            *reinterpret_cast<uint2 *>(dst + i) = v;
-                        }
-                    } else if constexpr ((CPW * 2) % 4 == 0) {
-#pragma unroll
-                        for (int i = 0; i < CPW; i += 2)
-                            if (i < ncw)
-                                *reinterpret_cast<uint32_t *>(dst + i) =
-                                    vals[k][i] | ((uint32_t)vals[k][i + 1] << 16);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < CPW; ++i)
-                            if (i < ncw) dst[i] = vals[k][i];
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < CPW; ++i) {
-                    if (i < ncw) {
-                        uint4 v;
-                        v.x = vals[0][i] | ((uint32_t)vals[1][i] << 16);
-                        v.y = vals[2][i] | ((uint32_t)vals[3][i] << 16);
-                        v.z = vals[4][i] | ((uint32_t)vals[5][i] << 16);
-                        v.w = vals[6][i] | ((uint32_t)vals[7][i] << 16);
-                        *reinterpret_cast<uint4 *>(Vt + (cbase + i) * VP + 8 * tg) = v;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- 2. S^T = K Q^T for two 32-token blocks
-        floatx16 s[2];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[tb][r] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const uint4 kv = *reinterpret_cast<const uint4 *>(Ks + (32 * tb + lr) * KP + 16 * ks + 8 * hf);
-                s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[ks], s[tb], 0, 0, 0);
-            }
-        }
-        // mask tokens past the window; tile max
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t tok = n0 + 32 * tb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                if (tok >= a.L_kv) s[tb][r] = -INFINITY;
-                mx = fmaxf(mx, s[tb][r]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * a.scale_log2);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+            for (int r = 0; r < 16; ++r) o[qb][d][r] = 0.0f;
+    float m_run[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.0f; }
 
-        bf16x8 pop[2][2];
+    const int L_kv = (int)a.L_kv;
+    const int nt = (L_kv + AT_NT - 1) / AT_NT;
+
+    // ---------------- items of 4 tokens: K items plane-fastest, V items
+    // token-fastest, which makes both LDS write patterns bank-conflict free
+    const uint32_t *plane[IPT];
+    const float *sbase[IPT];
+    int it_w[IPT], it_t4[IPT];
+    bool it_v[IPT], it_ok[IPT];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const float p = exp2f(__builtin_fmaf(s[tb][8 * hh + jj], a.scale_log2, -m_new));
-                    l_run += p;
-                    pop[tb][hh][jj] = (__bf16)p;
-                }
-            }
-        }
-        // ---- 3. O^T += V^T P^T
-#pragma unroll
-        for (int d = 0; d < DBLK; ++d) {
-            const uint16_t *vrow = Vt + (32 * d + lr) * VP + 4 * hf;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int tk = 32 * tb + 16 * hh;
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + tk);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + tk + 8);
-                    const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pop[tb][hh], o[d], 0, 0, 0);
-                }
-            }
-        }
+    for (int r = 0; r < IPT; ++r) {
+        const int it = tid + THREADS * r;
+        it_ok[r] = it < NITEMS;
+        const bool isV = it >= 16 * W;
+        const int j = isV ? it - 16 * W : it;
+        it_v[r] = isV;
+        it_w[r] = isV ? (j >> 4) : (j % W);
+        it_t4[r] = isV ? (j & 15) : (j / W);
+        if (!it_ok[r]) { it_w[r] = 0; it_t4[r] = 0; it_v[r] = false; }
+        plane[r] = (it_v[r] ? a.pv : a.pk) + ((int64_t)bh * W + it_w[r]) * a.L_cap + 4 * it_t4[r];
+        sbase[r] = (it_v[r] ? a.sv : a.sk) + (int64_t)bh * a.G_cap * D + it_w[r] * CPW;
     }
 
-    // ---- normalise and store
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.0f / l_tot;
-    if (qvalid) {
-        uint16_t *orow = a.out + (int64_t)b * a.so_b + qi * a.so_l + (int64_t)h * a.so_h;
+    uint32_t wd[IPT][4];
+    float sc[IPT][CPW];
+    int g_pref = 0;          // block of the prefetched tile's first token
+    bool split_pref = false; // the prefetched tile contains a block boundary
+
+    __syncthreads();   // off[] ready
+
+    // words of tile n0 (always in bounds: t + 4 <= L_cap) and, for a tile inside
+    // one block, that block's scales
+    auto prefetch = [&](int n0) {
+        g_pref = group_of(off, g_pref, n0);
+        split_pref = off[g_pref + 1] < min(n0 + AT_NT, L_kv);
 #pragma unroll
-        for (int d = 0; d < DBLK; ++d) {
+        for (int r = 0; r < IPT; ++r) {
+            if (!it_ok[r]) continue;
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(plane[r] + n0);
+            wd[r][0] = v0.x; wd[r][1] = v0.y; wd[r][2] = v0.z; wd[r][3] = v0.w;
+            const float *srow = sbase[r] + g_pref * D;
+            if constexpr (D % CPW == 0) {
+                // whole words only: the item's scales are one contiguous run
+                if constexpr (CPW % 4 == 0) {
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int c = 32 * d + 8 * r4 + 4 * hf;
-                uint2 v;
-                v.x = bf16_bits_rne(o[d][4 * r4] * inv) | (bf16_bits_rne(o[d][4 * r4 + 1] * inv) << 16);
-                v.y = bf16_bits_rne(o[d][4 * r4 + 2] * inv) | (bf16_bits_rne(o[d][4 * r4 + 3] * inv) << 16);
-                *reinterpret_cast<uint2 *>(orow + c) = v;
+                    for (int i = 0; i < CPW; i += 4) {
+                        const float4 v = *reinterpret_cast<const float4 *>(srow + i);
+                        sc[r][i] = v.x; sc[r][i + 1] = v.y; sc[r][i + 2] = v.z; sc[r][i + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < CPW; ++i) sc[r][i] = srow[i];
+                }
+            } else {
+                const int ncw = min(CPW, D - it_w[r] * CPW);
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) sc[r][i] = srow[min(i, ncw - 1)];
+            }
+        }
+    };
+
+    // dequantize the registers into LDS buffer `buf` (fast path: one block per tile)
+    auto dequant_fast = [&](int buf) {
+        uint16_t *K = Ks + buf * KBUF;
+        uint16_t *V = Vt + buf * VBUF;
+#pragma unroll
+        for (int r = 0; r < IPT; ++r) {
+            if (!it_ok[r]) continue;
+            const int w = it_w[r], t4 = it_t4[r];
+            const int cbase = w * CPW;
+            const int ncw = min(CPW, D - cbase);
+            if (it_v[r]) {
+                const int p0 = v_pos(4 * t4);
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
+                    if (i < ncw) {
+                        const float s = sc[r][i];
+                        uint2 lo;
+                        lo.x = pack_bf16x2(field_f32<BITS>(wd[r][0], i) * s, field_f32<BITS>(wd[r][1], i) * s);
+                        lo.y = pack_bf16x2(field_f32<BITS>(wd[r][2], i) * s, field_f32<BITS>(wd[r][3], i) * s);
+                        *reinterpret_cast<uint2 *>(V + (cbase + i) * VP + p0) = lo;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint16_t *dst = K + (4 * t4 + k) * KP + cbase;
+                    uint32_t pw[(CPW + 1) / 2];
+#pragma unroll
+                    for (int i = 0; i < CPW; i += 2) {
+                        const float v0 = field_f32<BITS>(wd[r][k], i) * sc[r][i];
+                        const float v1 = (i + 1 < CPW) ? field_f32<BITS>(wd[r][k], i + 1) * sc[r][i + 1] : 0.0f;
+                        pw[i / 2] = pack_bf16x2(v0, v1);
+                    }
+                    if constexpr (CPW % 8 == 0) {
+#pragma unroll
+                        for (int i = 0; i < CPW / 2; i += 4)
+                            *reinterpret_cast<uint4 *>(dst + 2 * i) = make_uint4(pw[i], pw[i + 1], pw[i + 2], pw[i + 3]);
+                    } else if constexpr (CPW % 4 == 0) {
+#pragma unroll
+                        for (int i = 0; i < CPW / 2; i += 2)
+                            *reinterpret_cast<uint2 *>(dst + 2 * i) = make_uint2(pw[i], pw[i + 1]);
+                    } else if constexpr (CPW % 2 == 0) {
+#pragma unroll
+                        for (int i = 0; i < CPW / 2; ++i)
+                            if (2 * i < ncw) *reinterpret_cast<uint32_t *>(dst + 2 * i) = pw[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < CPW; ++i)
+                            if (i < ncw) dst[i] = (uint16_t)(pw[i / 2] >> (16 * (i & 1)));
+                    }
+                }
+            }
+        }
+    };
+
+    // slow path for a tile that contains a block boundary: per-token scales
+    auto dequant_slow = [&](int buf, int n0) {
+        uint16_t *K = Ks + buf * KBUF;
+        uint16_t *V = Vt + buf * VBUF;
+#pragma unroll
+        for (int r = 0; r < IPT; ++r) {
+            if (!it_ok[r]) continue;
+            const int w = it_w[r], t4 = it_t4[r];
+            const int cbase = w * CPW;
+            const int ncw = min(CPW, D - cbase);
+            int g = group_of(off, 0, min(n0 + 4 * t4, L_kv - 1));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int t = min(n0 + 4 * t4 + k, L_kv - 1);
+                g = group_of(off, g, t);
+                const float *srow = sbase[r] + g * D;
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
+                    if (i < ncw) {
+                        const float v = field_f32<BITS>(wd[r][k], i) * srow[i];
+                        const uint16_t bits16 = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+                        if (it_v[r]) V[(cbase + i) * VP + v_pos(4 * t4 + k)] = bits16;
+                        else K[(4 * t4 + k) * KP + cbase + i] = bits16;
+                    }
+                }
+            }
+        }
+    };
+
+    const float c = a.scale_log2;
+
+    // one 64-token tile from LDS buffer `buf`
+    auto compute = [&](int buf, int n0, bool masked) {
+        const uint16_t *Kb = Ks + buf * KBUF + lr * KP + 8 * hf;
+        const uint16_t *Vb = Vt + buf * VBUF + lr * VP + 8 * hf;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            floatx16 s[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[qb][r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4 *>(Kb + 32 * tb * KP + 16 * ks));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][ks], s[qb], 0, 0, 0);
+            }
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int tok = n0 + 32 * tb + 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        if (tok >= L_kv) s[qb][r] = -INFINITY;
+                }
+            }
+            bf16x8 pop[QB][2];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float mx = fmaxf(s[qb][0], s[qb][1]);
+#pragma unroll
+                for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r], s[qb][r + 1]));
+                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                                 __builtin_bit_cast(uint32_t, mx), false, false);
+                // the swap returns the values of this lane's pair (lanes i and i^32)
+                mx = fmaxf(mx, fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
+                                     __builtin_bit_cast(float, (uint32_t)sw[1])));
+                const float mt = mx * c;
+                if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + AT_RESCALE_SLACK) != 0) {
+                    const float m_new = fmaxf(m_run[qb], mt);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+                    m_run[qb] = m_new;
+                    l_run[qb] *= alpha;
+#pragma unroll
+                    for (int d = 0; d < DBLK; ++d) scale_acc16(o[qb][d], alpha);
+                }
+                const float mneg = -m_run[qb];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    uint32_t u[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hh + 2 * e], c, mneg));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hh + 2 * e + 1], c, mneg));
+                        u[e] = pack_bf16x2(p0, p1);
+                        l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[e]), ones_bf16x2(),
+                                                                    l_run[qb], false);
+                    }
+                    pop[qb][hh] = as_bf16x8(make_uint4(u[0], u[1], u[2], u[3]));
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < DBLK; ++d) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const bf16x8 va = as_bf16x8(*reinterpret_cast<const uint4 *>(Vb + 32 * d * VP + 32 * tb + 16 * hh));
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        o[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qb][hh], o[qb][d], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // ---------------- pipeline: LDS-only barrier (global prefetches stay in flight)
+    auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    prefetch(0);
+    if (split_pref) dequant_slow(0, 0); else dequant_fast(0);
+    if (nt > 1) prefetch(AT_NT);
+    lds_barrier();
+    for (int jt = 0; jt + 1 < nt; ++jt) {
+        const int cur = jt & 1;
+        const int n0 = jt * AT_NT;
+        if (split_pref) dequant_slow(cur ^ 1, n0 + AT_NT);
+        else dequant_fast(cur ^ 1);
+        if (jt + 2 < nt) prefetch(n0 + 2 * AT_NT);
+        compute(cur, n0, false);
+        lds_barrier();
+    }
+    compute((nt - 1) & 1, (nt - 1) * AT_NT, true);
+
+    // ---------------- normalise and store
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qi = q_base + 32 * qb;
+        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+        const float inv = 1.0f / l_tot;
+        if (qi < a.Lq) {
+            uint16_t *orow = a.out + (int64_t)b * a.so_b + (int64_t)qi * a.so_l + (int64_t)h * a.so_h;
+#pragma unroll
+            for (int d = 0; d < DBLK; ++d) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int ch = 32 * d + 8 * r4 + 4 * hf;
+                    uint2 v;
+                    v.x = pack_bf16x2(o[qb][d][4 * r4] * inv, o[qb][d][4 * r4 + 1] * inv);
+                    v.y = pack_bf16x2(o[qb][d][4 * r4 + 2] * inv, o[qb][d][4 * r4 + 3] * inv);
+                    *reinterpret_cast<uint2 *>(orow + ch) = v;
+                }
             }
         }
     }
 }
 
+#ifndef VARQ_ATTN_QB
+#define VARQ_ATTN_QB 1
+#endif
+#ifndef VARQ_ATTN_NW
+#define VARQ_ATTN_NW 8
+#endif
+constexpr int AT_CFG_QB = VARQ_ATTN_QB;
+constexpr int AT_CFG_NW = VARQ_ATTN_NW;
+
 template <int BITS, int D>
 static hipError_t launch_at(const AttnArgs &a, hipStream_t st) {
     const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H;
     const int64_t grid = (n_blocks + 7) / 8 * 8;
-    hipLaunchKernelGGL((packed_attention_v1<BITS, D>), dim3((unsigned)grid), dim3(AT_THREADS), 0, st, a);
+    hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW>), dim3((unsigned)grid),
+                       dim3(64 * AT_CFG_NW), 0, st, a);
     return hipGetLastError();
 }
 
@@ -281,7 +439,7 @@ static hipError_t launch_at_bits(const AttnArgs &a, int bits, hipStream_t st) {
     }
 }
 
-int attention_q_tile() { return AT_QT; }
+int attention_q_tile() { return 32 * AT_CFG_QB * AT_CFG_NW; }
 
 hipError_t launch_packed_attention(const AttnArgs &a, int D, int bits, hipStream_t st) {
     if (D == 64) return launch_at_bits<64>(a, bits, st);
