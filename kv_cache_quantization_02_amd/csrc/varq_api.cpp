@@ -8,13 +8,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "../../include/varq.h"
 #include "varq_device.h"
 
 namespace varq {
-hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, hipStream_t st);
+hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, int grid, bool cooperative, hipStream_t st);
+int quant_pack_resident_blocks(int bits);
+int quant_pack_max_pack();
 hipError_t launch_unpack_dequant(const UnpackArgs &a, int bits, hipStream_t st);
 hipError_t launch_packed_attention(const AttnArgs &a, int D, int bits, hipStream_t st);
 int attention_q_tile();
@@ -72,13 +77,48 @@ int words_per_row(int D, int bits) {
     return (D + cpw - 1) / cpw;
 }
 
-int gcd(int x, int y) {
-    while (y) {
-        const int t = x % y;
-        x = y;
-        y = t;
+// Device scratch for quantize+pack's cross-work-group exchange, per (device,
+// stream). `sync` (epoch, finished count, status) is allocated once and zeroed;
+// the kernel leaves the count at zero and advances the epoch. `slots` grows on
+// demand and is zeroed when allocated; afterwards every slot the kernel reads
+// carries the epoch of the launch that wrote it, so stale contents never pass
+// for current ones, whatever the shapes of earlier calls.
+struct Scratch {
+    uint32_t *sync = nullptr;
+    uint64_t *slots = nullptr;
+    size_t n_slots = 0;
+};
+std::mutex g_scratch_mu;
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+int scratch_for(hipStream_t st, size_t n_slots, uint32_t **sync, uint64_t **slots) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack: no current device");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    Scratch &s = g_scratch[{dev, st}];
+    if (!s.sync) {
+        void *p = nullptr;
+        if (hipMalloc(&p, 4 * sizeof(uint32_t)) != hipSuccess || hipMemset(p, 0, 4 * sizeof(uint32_t)) != hipSuccess)
+            return fail(VARQ_ELAUNCH, "quantize_pack: scratch allocation failed");
+        s.sync = static_cast<uint32_t *>(p);
     }
-    return x;
+    if (s.n_slots < n_slots) {
+        if (s.slots) {
+            // the old buffer may still be in use by work queued on this stream
+            if (hipStreamSynchronize(st) != hipSuccess || hipFree(s.slots) != hipSuccess)
+                return fail(VARQ_ELAUNCH, "quantize_pack: cannot release scratch");
+            s.slots = nullptr;
+            s.n_slots = 0;
+        }
+        void *p = nullptr;
+        if (hipMalloc(&p, n_slots * 8) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack: scratch allocation failed");
+        if (hipMemset(p, 0, n_slots * 8) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack: scratch clear failed");
+        s.slots = static_cast<uint64_t *>(p);
+        s.n_slots = n_slots;
+    }
+    *sync = s.sync;
+    *slots = s.slots;
+    return VARQ_OK;
 }
 
 }  // namespace
@@ -137,29 +177,64 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
     a.scales = scales;
     a.L_cap = L_cap; a.tok_start = tok_start; a.G_cap = G_cap; a.group_start = group_start;
     a.B = B; a.H = H; a.D = D; a.G = G_in;
-    const int cpw = 32 / bits;
     a.W = words_per_row(D, bits);
-    // Slices of whole words whose first channel is a multiple of 8 (16-byte
-    // loads); sized so that one unit stays near 16K elements.
-    const int align_w = 8 / gcd(8, cpw);
-    const int64_t target = 16384;
-    int64_t units = 0;
+    // Units of at most T rows (T * D = the elements one work-group holds): a
+    // block longer than T is cut into chunks; shorter consecutive blocks are
+    // packed together, up to T rows and quant_pack_max_pack() blocks per unit.
+    const int lpr = D / 8;
+    const int T = (256 / lpr) * 8;
+    int tl = 0;
+    while ((1 << tl) < T) ++tl;
+    a.chunk_rows = T;
+    a.rows_log2 = tl;
+    const int max_pack = varq::quant_pack_max_pack();
+    int units = 0, max_nc = 1, pack_rows = 0, pack_blocks = 0;
+    bool in_pack = false;
     for (int g = 0; g < G_in; ++g) {
         a.off[g] = group_offsets[g];
-        const int64_t n = group_offsets[g + 1] - group_offsets[g];
-        int64_t sw = target / (n * cpw);
-        sw = (sw / align_w) * align_w;
-        if (sw < align_w) sw = align_w;
-        if (sw >= a.W) sw = a.W;
-        a.slice_words[g] = (uint8_t)sw;
-        a.unit_start[g] = (int32_t)units;
-        units += (int64_t)B * H * ((a.W + sw - 1) / sw);
+        const int n = group_offsets[g + 1] - group_offsets[g];
+        if (n > T) {
+            const int nc = (n + T - 1) / T;
+            a.unit_start[g] = units;
+            units += nc;
+            max_nc = std::max(max_nc, nc);
+            in_pack = false;
+        } else if (in_pack && pack_rows + n <= T && pack_blocks < max_pack) {
+            a.unit_start[g] = units - 1;
+            pack_rows += n;
+            ++pack_blocks;
+        } else {
+            a.unit_start[g] = units++;
+            in_pack = true;
+            pack_rows = n;
+            pack_blocks = 1;
+        }
     }
     a.off[G_in] = group_offsets[G_in];
-    a.unit_start[G_in] = (int32_t)units;
-    if (units >= (1LL << 31) - 8) return fail(VARQ_EINVAL, "quantize_pack: too many work units");
-    a.n_units = (int)units;
-    return launch_status(varq::launch_quant_pack(a, bits, static_cast<hipStream_t>(stream)), "quantize_pack");
+    a.unit_start[G_in] = units;
+    a.units_per_bh = units;
+    a.n_units = (int64_t)B * H * units;
+    const int resident = varq::quant_pack_resident_blocks(bits);
+    if (resident <= 0) return fail(VARQ_ELAUNCH, "quantize_pack: cannot query the device occupancy");
+    const int grid = (int)std::min<int64_t>(a.n_units, resident);
+    const bool split = max_nc > 1;
+    if (split) {
+        // chunks of one block wait for each other: all work-groups must be
+        // resident and no block may have more chunks than there are work-groups
+        if (max_nc > grid)
+            return fail(VARQ_EUNSUPPORTED, "quantize_pack: a block of %d chunks exceeds the %d resident work-groups",
+                        max_nc, grid);
+        const size_t bhg = (size_t)B * H * G_in;
+        uint32_t *sync = nullptr;
+        uint64_t *slots = nullptr;
+        if (int r = scratch_for(static_cast<hipStream_t>(stream), ((size_t)a.n_units + bhg) * D, &sync, &slots))
+            return r;
+        a.sync = sync;
+        a.part = slots;
+        a.fin = slots + (size_t)a.n_units * D;
+    }
+    return launch_status(varq::launch_quant_pack(a, bits, grid, split, static_cast<hipStream_t>(stream)),
+                         "quantize_pack");
 }
 
 int varq_unpack_dequant(const int32_t *packed, const float *scales,

@@ -13,20 +13,28 @@ namespace varq {
 
 // ---------------------------------------------------------------- arguments
 
-// quantize+pack. Work unit = (batch, head, block, channel slice); `unit_start`
-// is the prefix count of units per block, `slice_words` the words per slice of
-// each block (slices tile the W words of a row; the last one may be shorter).
+// quantize+pack. Work unit = up to chunk_rows token rows of one (batch, head):
+// a chunk of a block longer than chunk_rows, or a pack of whole consecutive
+// blocks. unit_start[g] is the index, within one (batch, head), of the first
+// unit holding block g (blocks of one pack share it); units_per_bh = unit_start[G].
+// When some block spans several chunks, `part`, `fin` and `sync` point to
+// scratch: 64-bit (epoch << 32 | fp32 bits) slots for per-unit partial maxima
+// [n_units, D] and block maxima [B*H*G, D], and sync = {epoch of the last
+// launch, work-groups finished, timeout status}. Otherwise part == nullptr.
 struct QuantPackArgs {
     const uint16_t *x;          // bf16 [B, L_in, H, D] at (sx_b, sx_l, sx_h), channel stride 1
     int64_t sx_b, sx_l, sx_h;
     uint32_t *packed;           // [B, H, W, L_cap]
     float *scales;              // [B, H, G_cap, D]
+    uint64_t *part;             // [n_units, D]
+    uint64_t *fin;              // [B*H*G, D]
+    uint32_t *sync;             // [3]
     int64_t L_cap, tok_start, G_cap, group_start;
+    int64_t n_units;
     int B, H, D, W, G;
-    int n_units;
+    int chunk_rows, rows_log2, units_per_bh;
     int32_t off[VARQ_MAX_GROUPS_DEV + 1];          // token offsets relative to x
-    int32_t unit_start[VARQ_MAX_GROUPS_DEV + 1];   // prefix of units per block
-    uint8_t slice_words[VARQ_MAX_GROUPS_DEV];      // words per slice, per block
+    int32_t unit_start[VARQ_MAX_GROUPS_DEV + 1];
 };
 
 struct UnpackArgs {

@@ -132,6 +132,35 @@ def test_quantize_pack_empty_and_deterministic(V):
     assert torch.equal(a1, a2) and torch.equal(s1, s2)
 
 
+def test_quantize_pack_shapes_alternate_on_one_stream(V):
+    """Calls of different shapes queued back to back share the stream's
+    scratch for the cross-work-group block maximum; blocks of up to 2000 rows
+    span several chunks. Every result must still be exact, and so must a call
+    on a second stream, which gets scratch of its own."""
+    _say("[qp alternating shapes]")
+    g = torch.Generator().manual_seed(7)
+    cases = []
+    for (B, H, D, off, bits) in [(2, 3, 64, [0, 5, 900, 2900], 3), (1, 5, 40, [0, 1201], 4),
+                                 (3, 2, 128, [0, 700, 701, 1800], 2), (2, 3, 64, [0, 333, 1201], 8),
+                                 (1, 1, 256, [0, 64, 1000], 6), (2, 3, 64, [0, 5, 900, 2900], 3)]:
+        x = (torch.randn(B, off[-1], H, D, generator=g) * 2).to(torch.bfloat16)
+        cases.append((x, off, bits))
+    outs = []
+    for (x, off, bits) in cases:                       # queued without synchronising
+        outs.append(_gpu_qp(V, x.to(DEV), off, bits))
+    side = torch.cuda.Stream()
+    x2, off2, bits2 = cases[0]
+    with torch.cuda.stream(side):
+        xd = x2.to(DEV)
+        pk2, sk2 = V.alloc_cache(x2.shape[0], x2.shape[2], x2.shape[3], off2[-1], len(off2) - 1, bits2, device=DEV)
+        V.quantize_pack(xd, off2, bits2, pk2, sk2, stream=side)
+    torch.cuda.synchronize()
+    for i, ((x, off, bits), (pk, sk)) in enumerate(zip(cases + [cases[0]], outs + [(pk2, sk2)])):
+        w, s = O.quantize_pack(x.float().numpy(), off, bits)
+        assert np.array_equal(_words(pk, off[-1]), w), f"words differ in call {i}"
+        assert np.array_equal(_f32bits(sk), s.view(np.uint32)), f"scales differ in call {i}"
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_quantize_pack_var_d30_full(V, bits):
     wl = WORKLOADS["var_d30"]
