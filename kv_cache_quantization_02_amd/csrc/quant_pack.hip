@@ -15,27 +15,28 @@
 // the fields are staged in LDS and stored plane by plane. Either way the lanes
 // of a work-group cover every token of the unit in each word plane.
 //
-// A block split over several chunks needs the maximum over all of them. Every
-// chunk but the last publishes its partial maxima in a scratch slot tagged with
-// this launch's epoch; the last chunk gathers them (waiting on each tag),
-// publishes the block maximum the same way and quantizes at once. The other
-// chunks defer their quantization: a work-group keeps the waiting unit in a
-// second register set, processes its next unit, and only then waits for the
-// block maximum. Each value crosses work-groups in one 64-bit atomic word that
-// carries both the tag and the maximum, so no cache flush or fence is needed
-// for it; the epoch advances once per launch, set by the last work-group to
-// finish.
+// A block split over several chunks needs the maximum over all of them. Each
+// chunk publishes its partial maxima in a scratch slot tagged with this
+// launch's epoch and is deferred: the work-group keeps its rows in registers
+// and goes on with its next unit. One unit later, the block's last chunk
+// gathers the partials (waiting on each tag), publishes the block maximum the
+// same way and is quantized; two units later every other chunk reads that
+// maximum and is quantized. Each value crosses work-groups in one 64-bit
+// atomic word carrying both the tag and the maximum, so no cache flush or
+// fence is needed for it; the epoch advances once per launch, set by the last
+// work-group to finish.
 //
-// Progress for the waits (such launches are cooperative: every work-group is
-// resident). Work-group w takes units w, w + grid, ...; for each unit u it
-// publishes P(u) (partial, or block maximum for a last chunk), then finishes
-// F(u') of the unit it deferred one step earlier. Let x be the smallest unit
-// whose P never happens. Before P(x) its work-group needs P(x - grid) and
-// F(x - 2 grid); the latter needs P of the last chunk of that unit's block,
-// which is < x when no block has more than grid chunks; and if x is a last
-// chunk it needs P of the earlier chunks of its block, all < x. So P(x)
-// happens, a contradiction; every F(u) then follows. Spins are nevertheless
-// bounded and report a timeout through a status word.
+// Progress (such launches are cooperative: every work-group is resident, and
+// no block has more chunks than there are work-groups, G). Work-group w takes
+// units w, w + G, ...; in the iteration of unit x it publishes x's partial
+// P(x) before anything that can wait, then gathers for the last chunk of
+// x - G and waits for the maximum of x - 2G. Let x be the smallest unit whose
+// P never happens. The gather for x - G needs P of chunks of its block, all
+// < x. The maximum for x - 2G is published in the iteration of r + G, r its
+// block's last chunk, r + G < x; that iteration's own gather needs P of units
+// < x, and the iterations before it in that work-group end by induction. So
+// P(x) happens, a contradiction; every gather and wait then ends. Spins are
+// nevertheless bounded and report a timeout through a status word.
 #include "varq_device.h"
 
 namespace varq {
@@ -44,7 +45,8 @@ constexpr int QP_THREADS = 256;
 constexpr int QP_ITEMS = 8;                                  // 16-byte row chunks held per thread
 constexpr int QP_UNIT_ELEMS = QP_THREADS * QP_ITEMS * 8;     // 16384 elements per unit
 constexpr int QP_MAX_PACK = 8;                               // blocks per packed unit
-constexpr int QP_SLOT_Y = QP_MAX_PACK;                       // scale slot of the deferred unit
+constexpr int QP_SLOT_R = QP_MAX_PACK;                       // scale slot of a last chunk
+constexpr int QP_SLOT_W = QP_MAX_PACK + 1;                   // scale slot of a waiting chunk
 constexpr unsigned QP_SPIN_LIMIT = 1u << 22;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -94,21 +96,44 @@ __device__ inline int local_block(const QuantPackArgs &a, const Unit &U, int r) 
     return lb;
 }
 
+// Work-group barrier that orders LDS only. __syncthreads() also waits for
+// every outstanding global load (vmcnt), which would drain the next unit's
+// prefetch at each barrier; no wave here reads global memory another wave of
+// its work-group wrote, so LDS ordering is all that is needed.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait for every outstanding global load (vmcnt(0)) before a unit's stores:
+// the next unit's prefetch has then landed, so the following loop iteration
+// does not also wait for these stores to be acknowledged.
+__device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 struct Lane {
     int chunk, rr, RP, lpr;
+    uint32_t xoff;      // byte offset of this lane's 16 bytes within a row
     bool active;
 };
 
 // Issue the 16-byte row-chunk loads of unit U into v (all in flight at once).
+// Loads are unconditional so that none waits for the one before it: rows past
+// the unit's end (and idle lanes) re-read its last row, which changes no
+// maximum and is never stored. Addresses are a wave-uniform base plus a 32-bit
+// lane offset (the host checks that a unit's rows span < 2^31 bytes).
 __device__ inline void load_unit(const QuantPackArgs &a, const Unit &U, uint4 (&v)[QP_ITEMS], const Lane &L) {
     const int64_t b = U.bh / a.H, h = U.bh - b * a.H;
-    const uint16_t *xbase = a.x + b * a.sx_b + h * a.sx_h + 8 * L.chunk + (int64_t)U.row0 * a.sx_l;
+    const char *ubase = reinterpret_cast<const char *>(a.x + b * a.sx_b + h * a.sx_h + (int64_t)U.row0 * a.sx_l);
+    const uint32_t row_bytes = (uint32_t)a.sx_l * 2u;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
-        const int r = L.rr + k * L.RP;
-        v[k] = make_uint4(0, 0, 0, 0);
-        if (L.active && r < U.n) v[k] = *reinterpret_cast<const uint4 *>(xbase + (int64_t)r * a.sx_l);
+        const int r = min(L.rr + k * L.RP, U.n - 1);
+        v[k] = *reinterpret_cast<const uint4 *>(ubase + (uint32_t)r * row_bytes + L.xoff);
     }
+}
+
+// Word plane p, unit row r of unit U: wave-uniform base plus a 32-bit lane
+// offset (the host checks that W * L_cap words span < 2^31 bytes).
+__device__ inline uint32_t *word_at(const QuantPackArgs &a, const Unit &U, int p, int r) {
+    char *base = reinterpret_cast<char *>(a.packed + U.bh * a.W * a.L_cap + a.tok_start + U.row0);
+    return reinterpret_cast<uint32_t *>(base + (uint32_t)(p * (uint32_t)a.L_cap + r) * 4u);
 }
 
 __device__ inline void flush_max(uint32_t *sh_max, int lb, int chunk, const u16x2 (&m)[4]) {
@@ -140,7 +165,7 @@ __device__ inline void unit_absmax(const QuantPackArgs &a, const Unit &U, const 
     for (int j = 0; j < 4; ++j) m[j] = u16x2{0, 0};
     if (U.nb == 1) {
 #pragma unroll
-        for (int k = 0; k < QP_ITEMS; ++k) absmax_item(m, v[k]);      // rows past n hold zeros
+        for (int k = 0; k < QP_ITEMS; ++k) absmax_item(m, v[k]);      // rows past n repeat row n-1
         flush_max(sh_max, 0, L.chunk, m);
         return;
     }
@@ -163,25 +188,29 @@ __device__ inline void unit_absmax(const QuantPackArgs &a, const Unit &U, const 
 }
 
 // b-bit two's complement fields (low bits of each word, higher bits garbage)
-// of the 8 channels in w under scales s8 and reciprocals y8.
-__device__ inline void codes8(const uint4 &w, const float (&s8)[8], const float (&y8)[8], bool fast,
-                              uint32_t (&f)[8]) {
+// of the 8 channels in w under scales s8 and reciprocals y8. FAST_ONLY: the
+// division-free quotient is exact for every scale here (the common case);
+// otherwise each channel picks it or IEEE division by its scale.
+template <bool FAST_ONLY>
+__device__ inline void codes8(const uint4 &w, const float (&s8)[8], const float (&y8)[8], uint32_t (&f)[8]) {
     const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float xl = bf16lo(wv[j]), xh = bf16hi(wv[j]);
-        if (fast) {
+        if (FAST_ONLY) {
             f[2 * j] = (uint32_t)code_fast(xl, s8[2 * j], y8[2 * j]);
             f[2 * j + 1] = (uint32_t)code_fast(xh, s8[2 * j + 1], y8[2 * j + 1]);
         } else {
-            f[2 * j] = (uint32_t)code_exact(xl, s8[2 * j]);
-            f[2 * j + 1] = (uint32_t)code_exact(xh, s8[2 * j + 1]);
+            f[2 * j] = (uint32_t)(fast_scale_ok(s8[2 * j]) ? code_fast(xl, s8[2 * j], y8[2 * j])
+                                                           : code_exact(xl, s8[2 * j]));
+            f[2 * j + 1] = (uint32_t)(fast_scale_ok(s8[2 * j + 1]) ? code_fast(xh, s8[2 * j + 1], y8[2 * j + 1])
+                                                                   : code_exact(xh, s8[2 * j + 1]));
         }
     }
 }
 
-__device__ inline void load_sy(const float *sh_s, const float *sh_y, int slot, int chunk, float (&s8)[8],
-                               float (&y8)[8], bool &fast) {
+__device__ inline bool load_sy(const float *sh_s, const float *sh_y, int slot, int chunk, float (&s8)[8],
+                               float (&y8)[8]) {
     const float4 *ps = reinterpret_cast<const float4 *>(sh_s + slot * 256 + 8 * chunk);
     const float4 *py = reinterpret_cast<const float4 *>(sh_y + slot * 256 + 8 * chunk);
     const float4 s0 = ps[0], s1 = ps[1], y0 = py[0], y1 = py[1];
@@ -189,9 +218,92 @@ __device__ inline void load_sy(const float *sh_s, const float *sh_y, int slot, i
     s8[4] = s1.x; s8[5] = s1.y; s8[6] = s1.z; s8[7] = s1.w;
     y8[0] = y0.x; y8[1] = y0.y; y8[2] = y0.z; y8[3] = y0.w;
     y8[4] = y1.x; y8[5] = y1.y; y8[6] = y1.z; y8[7] = y1.w;
-    fast = true;
+    bool fast = true;
 #pragma unroll
     for (int j = 0; j < 8; ++j) fast = fast && fast_scale_ok(s8[j]);
+    return fast;
+}
+
+// Fields of item k of unit U. SIMPLE: one block whose scales all allow the
+// division-free quotient, scales already in s8/y8. Otherwise the item's block
+// is looked up (packs) and each channel picks its quotient.
+template <bool SIMPLE>
+__device__ inline void item_codes(const QuantPackArgs &a, const Unit &U, const uint4 &w, const Lane &L, int r,
+                                  int slot, const float *sh_s, const float *sh_y, float (&s8)[8], float (&y8)[8],
+                                  int &cur, uint32_t (&f)[8]) {
+    if (SIMPLE) {
+        codes8<true>(w, s8, y8, f);
+    } else {
+        const int lb = U.nb > 1 ? local_block(a, U, r) : slot;
+        if (lb != cur) { load_sy(sh_s, sh_y, lb, L.chunk, s8, y8); cur = lb; }
+        codes8<false>(w, s8, y8, f);
+    }
+}
+
+// Words of unit U formed in registers, written to LDS as sh_w[plane * wp + row].
+template <int BITS, bool SIMPLE>
+__device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const uint4 (&v)[QP_ITEMS],
+                                   const Lane &L, int slot, const float *sh_s, const float *sh_y,
+                                   float (&s8)[8], float (&y8)[8], int cur, uint32_t *sh_w, int wp) {
+    constexpr uint32_t MASK = (1u << BITS) - 1u;
+#pragma unroll
+    for (int k = 0; k < QP_ITEMS; ++k) {
+        const int r = L.rr + k * L.RP;
+        const bool live = L.active && r < U.n;
+        uint32_t f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = 0;
+        if (SIMPLE) {
+            // rows past n repeat row n-1; their fields are discarded below
+            item_codes<true>(a, U, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, f);
+        } else if (live) {
+            item_codes<false>(a, U, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, f);
+        }
+        if constexpr (BITS == 4) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w |= (f[j] & MASK) << (4 * j);
+            if (live) sh_w[L.chunk * wp + r] = w;
+        } else if constexpr (BITS == 7 || BITS == 8) {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                w0 |= (f[j] & MASK) << (BITS * j);
+                w1 |= (f[4 + j] & MASK) << (BITS * j);
+            }
+            if (live) {
+                sh_w[(2 * L.chunk) * wp + r] = w0;
+                sh_w[(2 * L.chunk + 1) * wp + r] = w1;
+            }
+        } else if constexpr (BITS == 2) {
+            uint32_t half = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) half |= (f[j] & MASK) << (2 * j);
+            // chunk ^ 1 of the same row: lane tid ^ 1 (rows hold an even number of lanes)
+            const uint32_t other = (uint32_t)__shfl_xor((int)half, 1);
+            if (live && (L.chunk & 1) == 0) sh_w[(L.chunk >> 1) * wp + r] = half | (other << 16);
+        }
+    }
+}
+
+template <int BITS, bool SIMPLE>
+__device__ inline void stage_codes(const QuantPackArgs &a, const Unit &U, const uint4 (&v)[QP_ITEMS],
+                                   const Lane &L, int slot, const float *sh_s, const float *sh_y,
+                                   float (&s8)[8], float (&y8)[8], int cur, uint8_t *sh_codes, int pitch) {
+    constexpr uint32_t MASK = (1u << BITS) - 1u;
+#pragma unroll
+    for (int k = 0; k < QP_ITEMS; ++k) {
+        const int r = L.rr + k * L.RP;
+        if (L.active && r < U.n) {
+            uint32_t f[8];
+            item_codes<SIMPLE>(a, U, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, f);
+            uint8_t *dst = sh_codes + r * pitch + 8 * L.chunk;
+            *reinterpret_cast<uint32_t *>(dst) =
+                (f[0] & MASK) | ((f[1] & MASK) << 8) | ((f[2] & MASK) << 16) | ((f[3] & MASK) << 24);
+            *reinterpret_cast<uint32_t *>(dst + 4) =
+                (f[4] & MASK) | ((f[5] & MASK) << 8) | ((f[6] & MASK) << 16) | ((f[7] & MASK) << 24);
+        }
+    }
 }
 
 // Quantize and store unit U (rows in v) with the scales of LDS slot `slot`
@@ -202,86 +314,47 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
                                      const Lane &L, int slot, const float *sh_s, const float *sh_y,
                                      uint8_t *sh_codes) {
     constexpr int CPW = 32 / BITS;
-    constexpr uint32_t MASK = (1u << BITS) - 1u;
     const int tid = threadIdx.x;
     const int D = a.D;
-    uint32_t *plane0 = a.packed + U.bh * a.W * a.L_cap + a.tok_start + U.row0;
     // a 2-bit word takes a lane pair (16 channels); with an odd lane count per
     // row the last chunk has no partner, so that case is staged in LDS like
     // 3, 5 and 6 bits
     const bool direct = (BITS == 4 || BITS == 7 || BITS == 8) || (BITS == 2 && (L.lpr & 1) == 0);
 
+    // wave-uniform choice of the common path: one block, every scale of the
+    // wave's channels allows the division-free quotient
     float s8[8], y8[8];
     bool fast = true;
-    int cur = -1;
-    if (U.nb == 1 && L.active) { load_sy(sh_s, sh_y, slot, L.chunk, s8, y8, fast); cur = slot; }
+    if (U.nb == 1 && L.active) fast = load_sy(sh_s, sh_y, slot, L.chunk, s8, y8);
+    const bool simple = U.nb == 1 && __all(fast);
+    const int cur = U.nb == 1 ? slot : -1;
 
+    const int tshift = a.rows_log2;
+    const int span = 1 << tshift;
     if (direct) {
-#pragma unroll
-        for (int k = 0; k < QP_ITEMS; ++k) {
-            const int r = L.rr + k * L.RP;
-            const bool live = L.active && r < U.n;
-            uint32_t f[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) f[j] = 0;
-            if (live) {
-                if (U.nb > 1) {
-                    const int lb = local_block(a, U, r);
-                    if (lb != cur) { load_sy(sh_s, sh_y, lb, L.chunk, s8, y8, fast); cur = lb; }
-                }
-                codes8(v[k], s8, y8, fast, f);
-            }
-            if constexpr (BITS == 4) {
-                uint32_t w = 0;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) w |= (f[j] & MASK) << (4 * j);
-                if (live) plane0[(int64_t)L.chunk * a.L_cap + r] = w;
-            } else if constexpr (BITS == 7 || BITS == 8) {
-                uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    w0 |= (f[j] & MASK) << (BITS * j);
-                    w1 |= (f[4 + j] & MASK) << (BITS * j);
-                }
-                if (live) {
-                    plane0[(int64_t)(2 * L.chunk) * a.L_cap + r] = w0;
-                    plane0[(int64_t)(2 * L.chunk + 1) * a.L_cap + r] = w1;
-                }
-            } else if constexpr (BITS == 2) {
-                uint32_t half = 0;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) half |= (f[j] & MASK) << (2 * j);
-                // chunk ^ 1 of the same row: lane tid ^ 1 (rows hold an even number of lanes)
-                const uint32_t other = (uint32_t)__shfl_xor((int)half, 1);
-                if (live && (L.chunk & 1) == 0) plane0[(int64_t)(L.chunk >> 1) * a.L_cap + r] = half | (other << 16);
-            }
+        // words -> LDS planes -> global, consecutive lanes on consecutive
+        // tokens of a plane. Plane pitch T + 64/lanes-per-row: the lanes of a
+        // wave (chunks x rows) then write distinct banks.
+        uint32_t *sh_w = reinterpret_cast<uint32_t *>(sh_codes);
+        const int wp = a.chunk_rows + 64 / L.lpr;
+        if (simple) stage_words<BITS, true>(a, U, v, L, slot, sh_s, sh_y, s8, y8, cur, sh_w, wp);
+        else stage_words<BITS, false>(a, U, v, L, slot, sh_s, sh_y, s8, y8, cur, sh_w, wp);
+        lds_barrier();
+        wait_loads();
+        for (int i = tid; i < a.W * span; i += QP_THREADS) {
+            const int w = i >> tshift, r = i & (span - 1);
+            if (r < U.n) *word_at(a, U, w, r) = sh_w[w * wp + r];
         }
-        __syncthreads();
+        lds_barrier();
         return;
     }
 
     // ---- fields -> LDS code rows -> words, one plane at a time
     const int pitch = D >= 64 ? D + 4 : D;
-#pragma unroll
-    for (int k = 0; k < QP_ITEMS; ++k) {
-        const int r = L.rr + k * L.RP;
-        if (L.active && r < U.n) {
-            if (U.nb > 1) {
-                const int lb = local_block(a, U, r);
-                if (lb != cur) { load_sy(sh_s, sh_y, lb, L.chunk, s8, y8, fast); cur = lb; }
-            }
-            uint32_t f[8];
-            codes8(v[k], s8, y8, fast, f);
-            uint8_t *dst = sh_codes + r * pitch + 8 * L.chunk;
-            *reinterpret_cast<uint32_t *>(dst) =
-                (f[0] & MASK) | ((f[1] & MASK) << 8) | ((f[2] & MASK) << 16) | ((f[3] & MASK) << 24);
-            *reinterpret_cast<uint32_t *>(dst + 4) =
-                (f[4] & MASK) | ((f[5] & MASK) << 8) | ((f[6] & MASK) << 16) | ((f[7] & MASK) << 24);
-        }
-    }
-    __syncthreads();
-    const int tshift = a.rows_log2;
-    const int span = 1 << tshift;
+    if (simple) stage_codes<BITS, true>(a, U, v, L, slot, sh_s, sh_y, s8, y8, cur, sh_codes, pitch);
+    else stage_codes<BITS, false>(a, U, v, L, slot, sh_s, sh_y, s8, y8, cur, sh_codes, pitch);
+    lds_barrier();
+    wait_loads();
     for (int i = tid; i < a.W * span; i += QP_THREADS) {
         const int w = i >> tshift, r = i & (span - 1);
         if (r >= U.n) continue;
@@ -294,34 +367,72 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
         } else {
             for (int q = 0; q < D - cw0; ++q) word |= (uint32_t)src[q] << (q * BITS);
         }
-        plane0[(int64_t)w * a.L_cap + r] = word;
+        *word_at(a, U, w, r) = word;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 __device__ inline uint64_t tagged(uint32_t epoch, float m) { return ((uint64_t)epoch << 32) | f2u(m); }
 
-// Wait until the 64-bit slot carries `epoch`; returns the maximum it holds.
-__device__ inline float wait_slot(const uint64_t *p, uint32_t epoch, uint32_t *status) {
+__device__ inline uint64_t load_slot(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The maximum held by slot p, whose last load returned v, once the slot
+// carries `epoch` (spins until then; a timeout is recorded in *status).
+__device__ inline float slot_max(const uint64_t *p, uint64_t v, uint32_t epoch, uint32_t *status) {
     unsigned spins = 0;
-    uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while ((uint32_t)(v >> 32) != epoch) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins > QP_SPIN_LIMIT) {
             __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
-        v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = load_slot(p);
     }
     return u2f((uint32_t)v);
 }
 
+// Maximum of m and the partial maxima of chunks 0 .. n-1 starting at slot p
+// (stride D), eight loads in flight at a time.
+__device__ inline float gather_partials(const uint64_t *p, int n, int D, float m, uint32_t epoch, uint32_t *status) {
+    for (int c0 = 0; c0 < n; c0 += 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (c0 + j < n) v[j] = load_slot(p + (int64_t)(c0 + j) * D);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (c0 + j < n) m = fmaxf(m, slot_max(p + (int64_t)(c0 + j) * D, v[j], epoch, status));
+    }
+    return m;
+}
+
+// Scale and reciprocal of maximum m into LDS slot `slot` (thread = channel).
+template <int BITS>
+__device__ inline float put_scale(float *sh_s, float *sh_y, int slot, int tid, float m) {
+    constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
+    const float s = m / QMAX;                                       // IEEE fp32 division
+    sh_s[slot * 256 + tid] = s;
+    sh_y[slot * 256 + tid] = recip_for_codes(s);
+    return s;
+}
+
+__device__ inline float *scale_ptr(const QuantPackArgs &a, const Unit &U, int tid) {
+    return a.scales + (U.bh * a.G_cap + a.group_start + U.g0) * a.D + tid;
+}
+
+template <int N>
+__device__ inline void copy_regs(uint4 (&dst)[N], const uint4 (&src)[N]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) dst[k] = src[k];
+}
+
 template <int BITS>
 __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPackArgs a) {
-    constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
     __shared__ __attribute__((aligned(16))) uint32_t sh_max[QP_MAX_PACK * 256];
-    __shared__ __attribute__((aligned(16))) float sh_s[(QP_MAX_PACK + 1) * 256];
-    __shared__ __attribute__((aligned(16))) float sh_y[(QP_MAX_PACK + 1) * 256];
+    __shared__ __attribute__((aligned(16))) float sh_s[(QP_MAX_PACK + 2) * 256];
+    __shared__ __attribute__((aligned(16))) float sh_y[(QP_MAX_PACK + 2) * 256];
     __shared__ __attribute__((aligned(16))) uint8_t sh_codes[QP_UNIT_ELEMS + 4 * 512];
 
     const int tid = threadIdx.x;
@@ -332,8 +443,10 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
     L.chunk = tid % L.lpr;
     L.rr = tid / L.lpr;
     L.active = L.rr < L.RP;
+    L.xoff = (uint32_t)(8 * L.chunk) * 2u;
     const int64_t step = gridDim.x;
     const bool split = a.part != nullptr;     // some block spans several chunks
+    uint32_t *status = a.sync + 2;
 
     uint32_t epoch = 0;
     if (split) {
@@ -341,87 +454,101 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
         if (epoch == 0) epoch = 1;
     }
     for (int i = tid; i < QP_MAX_PACK * 256; i += QP_THREADS) sh_max[i] = 0;
-    __syncthreads();
+    lds_barrier();
 
-    uint4 X[QP_ITEMS], Y[QP_ITEMS], Z[QP_ITEMS];
-    Unit UX, UY, UZ;
-    bool pendY = false;
+    // Per unit X: absmax; a chunk of a split block publishes its partial and
+    // is deferred. One unit later a last chunk gathers its block's partials,
+    // publishes the block maximum and is quantized; two units later any other
+    // chunk reads that maximum and is quantized. Units of whole blocks are
+    // quantized at once. The next unit's loads are issued after the exchange's
+    // loads (loads complete in issue order) and stay in flight while the
+    // ready units are quantized.
+    uint4 X[QP_ITEMS], Z[QP_ITEMS], D1[QP_ITEMS], D2[QP_ITEMS];
+    Unit UX, UZ, U1 = {}, U2 = {};
+    bool has1 = false, has2 = false;          // D1: deferred one unit ago; D2: two units ago
     int64_t u = blockIdx.x;
     if (u < a.n_units) { UZ = unit_of(a, u); load_unit(a, UZ, Z, L); }
     while (u < a.n_units) {
         UX = UZ;
-#pragma unroll
-        for (int k = 0; k < QP_ITEMS; ++k) X[k] = Z[k];
+        copy_regs(X, Z);
         u += step;
-        if (u < a.n_units) { UZ = unit_of(a, u); load_unit(a, UZ, Z, L); }
+        const bool last1 = has1 && U1.c == U1.nc - 1;
 
-        // ---- absmax of X; a split block's chunks exchange maxima
+        // block maximum for D2, published by its block's last chunk
+        const uint64_t *fin2 = a.fin + (U2.bh * a.G + U2.g0) * D + tid;
+        uint64_t v2 = 0;
+        if (has2 && tid < D) v2 = load_slot(fin2);
+
         unit_absmax(a, UX, X, L, sh_max);
-        __syncthreads();
-        const bool deferX = UX.nc > 1 && UX.c < UX.nc - 1;
-        float m0 = 0.0f;
+        lds_barrier();
+        const bool splitX = UX.nc > 1;
         if (tid < D) {
-            m0 = u2f(sh_max[tid]);
-            if (UX.nc > 1) {
-                if (deferX) {
-                    __hip_atomic_store(a.part + UX.id * D + tid, tagged(epoch, m0), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                } else {
-                    for (int cc = 0; cc < UX.nc - 1; ++cc)
-                        m0 = fmaxf(m0, wait_slot(a.part + (UX.id - UX.c + cc) * D + tid, epoch, a.sync + 2));
-                    __hip_atomic_store(a.fin + (UX.bh * a.G + UX.g0) * D + tid, tagged(epoch, m0),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-        }
-
-        // ---- scales: the deferred unit Y (block maximum from its last chunk),
-        // and X unless X waits now; the block maxima in LDS are cleared for the
-        // next unit (the barrier below orders that before its max-atomics)
-        if (tid < D) {
-            if (pendY) {
-                const float m = wait_slot(a.fin + (UY.bh * a.G + UY.g0) * D + tid, epoch, a.sync + 2);
-                const float s = m / QMAX;                            // IEEE fp32 division
-                sh_s[QP_SLOT_Y * 256 + tid] = s;
-                sh_y[QP_SLOT_Y * 256 + tid] = recip_for_codes(s);
-            }
+            const float m0 = u2f(sh_max[tid]);
             sh_max[tid] = 0;
-            if (!deferX) {
-                float *scl = a.scales + (UX.bh * a.G_cap + a.group_start + UX.g0) * D + tid;
+            if (splitX) {
+                __hip_atomic_store(a.part + UX.id * D + tid, tagged(epoch, m0), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                // whole blocks: scales now; block maxima in LDS are cleared
+                // for the next unit (ordered before its atomics by the barrier)
+                float *scl = scale_ptr(a, UX, tid);
                 for (int lb = 0; lb < UX.nb; ++lb) {
                     float m = m0;
                     if (lb > 0) {
                         m = u2f(sh_max[lb * 256 + tid]);
                         sh_max[lb * 256 + tid] = 0;
                     }
-                    const float s = m / QMAX;                        // IEEE fp32 division
-                    sh_s[lb * 256 + tid] = s;
-                    sh_y[lb * 256 + tid] = recip_for_codes(s);
-                    scl[(int64_t)lb * D] = s;
+                    scl[(int64_t)lb * D] = put_scale<BITS>(sh_s, sh_y, lb, tid, m);
                 }
             }
+            if (last1) {
+                const float m = gather_partials(a.part + (U1.id - U1.c) * D + tid, U1.nc, D, 0.0f, epoch, status);
+                __hip_atomic_store(a.fin + (U1.bh * a.G + U1.g0) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, tid, m);
+            }
+            if (has2) put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin2, v2, epoch, status));
         }
-        __syncthreads();
-        if (pendY) quantize_unit<BITS>(a, UY, Y, L, QP_SLOT_Y, sh_s, sh_y, sh_codes);
-        if (!deferX) {
-            quantize_unit<BITS>(a, UX, X, L, 0, sh_s, sh_y, sh_codes);
-            pendY = false;
-        } else {
-            UY = UX;
-#pragma unroll
-            for (int k = 0; k < QP_ITEMS; ++k) Y[k] = X[k];
-            pendY = true;
-        }
+        if (u < a.n_units) { UZ = unit_of(a, u); load_unit(a, UZ, Z, L); }
+        lds_barrier();
+        if (has2) quantize_unit<BITS>(a, U2, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
+        if (last1) quantize_unit<BITS>(a, U1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
+        if (!splitX) quantize_unit<BITS>(a, UX, X, L, 0, sh_s, sh_y, sh_codes);
+        // advance the deferral pipeline
+        has2 = has1 && !last1;
+        if (has2) { U2 = U1; copy_regs(D2, D1); }
+        has1 = splitX;
+        if (has1) { U1 = UX; copy_regs(D1, X); }
     }
-    if (pendY) {
+
+    // drain: a deferred last chunk first (its maximum may be awaited), then
+    // the waiting chunks
+    if (has1 && U1.c == U1.nc - 1) {
         if (tid < D) {
-            const float m = wait_slot(a.fin + (UY.bh * a.G + UY.g0) * D + tid, epoch, a.sync + 2);
-            const float s = m / QMAX;
-            sh_s[QP_SLOT_Y * 256 + tid] = s;
-            sh_y[QP_SLOT_Y * 256 + tid] = recip_for_codes(s);
+            const float m = gather_partials(a.part + (U1.id - U1.c) * D + tid, U1.nc, D, 0.0f, epoch, status);
+            __hip_atomic_store(a.fin + (U1.bh * a.G + U1.g0) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, tid, m);
         }
-        __syncthreads();
-        quantize_unit<BITS>(a, UY, Y, L, QP_SLOT_Y, sh_s, sh_y, sh_codes);
+        lds_barrier();
+        quantize_unit<BITS>(a, U1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
+        has1 = false;
+    }
+    if (has2) {
+        if (tid < D) {
+            const uint64_t *fin2 = a.fin + (U2.bh * a.G + U2.g0) * D + tid;
+            put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin2, load_slot(fin2), epoch, status));
+        }
+        lds_barrier();
+        quantize_unit<BITS>(a, U2, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
+    }
+    if (has1) {
+        if (tid < D) {
+            const uint64_t *fin1 = a.fin + (U1.bh * a.G + U1.g0) * D + tid;
+            put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin1, load_slot(fin1), epoch, status));
+        }
+        lds_barrier();
+        quantize_unit<BITS>(a, U1, D1, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
     }
 
     // ---- the last work-group to finish advances the epoch for the next launch

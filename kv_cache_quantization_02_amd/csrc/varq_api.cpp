@@ -210,6 +210,12 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
             pack_blocks = 1;
         }
     }
+    // the kernel addresses a unit's rows and a (batch, head)'s word planes with
+    // 32-bit byte offsets
+    if ((int64_t)T * sx_l * 2 >= ((int64_t)1 << 31) || (int64_t)a.W * L_cap * 4 >= ((int64_t)1 << 31))
+        return fail(VARQ_EUNSUPPORTED,
+                    "quantize_pack: token stride %lld or cache length %lld too large for 32-bit offsets",
+                    (long long)sx_l, (long long)L_cap);
     a.off[G_in] = group_offsets[G_in];
     a.unit_start[G_in] = units;
     a.units_per_bh = units;
