@@ -33,6 +33,7 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int AT_NT = 64;        // KV tokens per tile
+constexpr int AT_SL_MAXG = 32;   // blocks whose K and V scales a work-group can hold in LDS
 constexpr float AT_RESCALE_SLACK = 8.0f;   // log2 units: p <= 2^8 between rescales
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -87,7 +88,10 @@ __device__ inline int v_pos(int tok) {
     return (tok & ~15) + 4 * (((q & 1) << 1) | (q >> 1)) + (tok & 3);
 }
 
-template <int BITS, int D, int QB, int NW>
+// SL: the (batch, head)'s K and V scales (at most AT_SL_MAXG blocks) are
+// copied to LDS once, and dequantization reads them there; otherwise each
+// tile's scales are prefetched from memory with its words.
+template <int BITS, int D, int QB, int NW, bool SL>
 __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a) {
     using T = AttnTile<BITS, D, QB, NW>;
     constexpr int CPW = T::CPW, W = T::W, KP = T::KP, VP = T::VP;
@@ -96,10 +100,12 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
     constexpr int KBUF = AT_NT * KP, VBUF = D * VP;
+    constexpr bool DEEP = false;
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
     __shared__ int32_t off[VARQ_MAX_GROUPS_DEV + 1];
+    __shared__ __attribute__((aligned(16))) float sS[SL ? 2 * AT_SL_MAXG * D : 4];   // K rows, then V rows
 
     const int n_blocks = a.n_qtiles * a.B * a.H;
     const int lid = (int)xcd_logical_id(blockIdx.x, n_blocks);
@@ -113,6 +119,13 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     const int lr = lane & 31, hf = lane >> 5;
 
     for (int i = tid; i <= a.G; i += THREADS) off[i] = a.off[i];
+    if constexpr (SL) {
+        const float4 *gk = reinterpret_cast<const float4 *>(a.sk + (int64_t)bh * a.G_cap * D);
+        const float4 *gv = reinterpret_cast<const float4 *>(a.sv + (int64_t)bh * a.G_cap * D);
+        float4 *lk = reinterpret_cast<float4 *>(sS);
+        float4 *lv = reinterpret_cast<float4 *>(sS + AT_SL_MAXG * D);
+        for (int i = tid; i < a.G * (D / 4); i += THREADS) { lk[i] = gk[i]; lv[i] = gv[i]; }
+    }
 
     // Q^T operands: lane = query, slots (hf, j) = channel 16*ks + 8*hf + j
     const int q_base = qt * QT + wave * QW + lr;
@@ -168,122 +181,176 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         sbase[r] = (it_v[r] ? a.sv : a.sk) + (int64_t)bh * a.G_cap * D + it_w[r] * CPW;
     }
 
-    uint32_t wd[IPT][4];
-    float sc[IPT][CPW];
-    int g_pref = 0;          // block of the prefetched tile's first token
-    bool split_pref = false; // the prefetched tile contains a block boundary
+    // Prefetched tile: words per item and, when the tile lies in one block and
+    // scales are not in LDS, that block's scales for the item's channels. Two
+    // sets alternate so that a tile's loads are issued two tiles ahead.
+    struct Pref {
+        uint32_t wd[IPT][4];
+        float sc[IPT][CPW];
+        int g;        // block of the tile's first token
+        bool split;   // the tile contains a block boundary
+    };
+    Pref P0, P1;
+    P0.g = P1.g = 0;
+    P0.split = P1.split = false;
+    int g_run = 0;    // search hint: block of the last prefetched tile
 
-    __syncthreads();   // off[] ready
+    __syncthreads();   // off[] (and scales in LDS) ready
 
     // words of tile n0 (always in bounds: t + 4 <= L_cap) and, for a tile inside
     // one block, that block's scales
-    auto prefetch = [&](int n0) {
-        g_pref = group_of(off, g_pref, n0);
-        split_pref = off[g_pref + 1] < min(n0 + AT_NT, L_kv);
+    auto prefetch = [&](Pref &P, int n0) {
+        g_run = group_of(off, g_run, n0);
+        P.g = g_run;
+        P.split = off[g_run + 1] < min(n0 + AT_NT, L_kv);
 #pragma unroll
         for (int r = 0; r < IPT; ++r) {
             if (!it_ok[r]) continue;
             const uint4 v0 = *reinterpret_cast<const uint4 *>(plane[r] + n0);
-            wd[r][0] = v0.x; wd[r][1] = v0.y; wd[r][2] = v0.z; wd[r][3] = v0.w;
-            const float *srow = sbase[r] + g_pref * D;
+            P.wd[r][0] = v0.x; P.wd[r][1] = v0.y; P.wd[r][2] = v0.z; P.wd[r][3] = v0.w;
+            if constexpr (SL) continue;
+            const float *srow = sbase[r] + P.g * D;
             if constexpr (D % CPW == 0) {
                 // whole words only: the item's scales are one contiguous run
                 if constexpr (CPW % 4 == 0) {
 #pragma unroll
                     for (int i = 0; i < CPW; i += 4) {
                         const float4 v = *reinterpret_cast<const float4 *>(srow + i);
-                        sc[r][i] = v.x; sc[r][i + 1] = v.y; sc[r][i + 2] = v.z; sc[r][i + 3] = v.w;
+                        P.sc[r][i] = v.x; P.sc[r][i + 1] = v.y; P.sc[r][i + 2] = v.z; P.sc[r][i + 3] = v.w;
                     }
                 } else {
 #pragma unroll
-                    for (int i = 0; i < CPW; ++i) sc[r][i] = srow[i];
+                    for (int i = 0; i < CPW; ++i) P.sc[r][i] = srow[i];
                 }
             } else {
                 const int ncw = min(CPW, D - it_w[r] * CPW);
 #pragma unroll
-                for (int i = 0; i < CPW; ++i) sc[r][i] = srow[min(i, ncw - 1)];
+                for (int i = 0; i < CPW; ++i) P.sc[r][i] = srow[min(i, ncw - 1)];
             }
         }
     };
 
-    // dequantize the registers into LDS buffer `buf` (fast path: one block per tile)
-    auto dequant_fast = [&](int buf) {
+    // item r of a prefetched tile into LDS buffer `buf`; scale of code i of
+    // token k is sk(k, i)
+    auto dequant_item = [&](int buf, const Pref &P, int r, auto sk) {
         uint16_t *K = Ks + buf * KBUF;
         uint16_t *V = Vt + buf * VBUF;
+        const int w = it_w[r], t4 = it_t4[r];
+        const int cbase = w * CPW;
+        const int ncw = min(CPW, D - cbase);
+        if (it_v[r]) {
+            const int p0 = v_pos(4 * t4);
 #pragma unroll
-        for (int r = 0; r < IPT; ++r) {
-            if (!it_ok[r]) continue;
-            const int w = it_w[r], t4 = it_t4[r];
-            const int cbase = w * CPW;
-            const int ncw = min(CPW, D - cbase);
-            if (it_v[r]) {
-                const int p0 = v_pos(4 * t4);
-#pragma unroll
-                for (int i = 0; i < CPW; ++i) {
-                    if (i < ncw) {
-                        const float s = sc[r][i];
-                        uint2 lo;
-                        lo.x = pack_bf16x2(field_f32<BITS>(wd[r][0], i) * s, field_f32<BITS>(wd[r][1], i) * s);
-                        lo.y = pack_bf16x2(field_f32<BITS>(wd[r][2], i) * s, field_f32<BITS>(wd[r][3], i) * s);
-                        *reinterpret_cast<uint2 *>(V + (cbase + i) * VP + p0) = lo;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    uint16_t *dst = K + (4 * t4 + k) * KP + cbase;
-                    uint32_t pw[(CPW + 1) / 2];
-#pragma unroll
-                    for (int i = 0; i < CPW; i += 2) {
-                        const float v0 = field_f32<BITS>(wd[r][k], i) * sc[r][i];
-                        const float v1 = (i + 1 < CPW) ? field_f32<BITS>(wd[r][k], i + 1) * sc[r][i + 1] : 0.0f;
-                        pw[i / 2] = pack_bf16x2(v0, v1);
-                    }
-                    if constexpr (CPW % 8 == 0) {
-#pragma unroll
-                        for (int i = 0; i < CPW / 2; i += 4)
-                            *reinterpret_cast<uint4 *>(dst + 2 * i) = make_uint4(pw[i], pw[i + 1], pw[i + 2], pw[i + 3]);
-                    } else if constexpr (CPW % 4 == 0) {
-#pragma unroll
-                        for (int i = 0; i < CPW / 2; i += 2)
-                            *reinterpret_cast<uint2 *>(dst + 2 * i) = make_uint2(pw[i], pw[i + 1]);
-                    } else if constexpr (CPW % 2 == 0) {
-#pragma unroll
-                        for (int i = 0; i < CPW / 2; ++i)
-                            if (2 * i < ncw) *reinterpret_cast<uint32_t *>(dst + 2 * i) = pw[i];
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < CPW; ++i)
-                            if (i < ncw) dst[i] = (uint16_t)(pw[i / 2] >> (16 * (i & 1)));
-                    }
+            for (int i = 0; i < CPW; ++i) {
+                if (i < ncw) {
+                    uint2 lo;
+                    lo.x = pack_bf16x2(field_f32<BITS>(P.wd[r][0], i) * sk(0, i), field_f32<BITS>(P.wd[r][1], i) * sk(1, i));
+                    lo.y = pack_bf16x2(field_f32<BITS>(P.wd[r][2], i) * sk(2, i), field_f32<BITS>(P.wd[r][3], i) * sk(3, i));
+                    *reinterpret_cast<uint2 *>(V + (cbase + i) * VP + p0) = lo;
                 }
             }
-        }
-    };
-
-    // slow path for a tile that contains a block boundary: per-token scales
-    auto dequant_slow = [&](int buf, int n0) {
-        uint16_t *K = Ks + buf * KBUF;
-        uint16_t *V = Vt + buf * VBUF;
-#pragma unroll
-        for (int r = 0; r < IPT; ++r) {
-            if (!it_ok[r]) continue;
-            const int w = it_w[r], t4 = it_t4[r];
-            const int cbase = w * CPW;
-            const int ncw = min(CPW, D - cbase);
-            int g = group_of(off, 0, min(n0 + 4 * t4, L_kv - 1));
+        } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int t = min(n0 + 4 * t4 + k, L_kv - 1);
-                g = group_of(off, g, t);
-                const float *srow = sbase[r] + g * D;
+                uint16_t *dst = K + (4 * t4 + k) * KP + cbase;
+                uint32_t pw[(CPW + 1) / 2];
 #pragma unroll
-                for (int i = 0; i < CPW; ++i) {
-                    if (i < ncw) {
-                        const float v = field_f32<BITS>(wd[r][k], i) * srow[i];
-                        const uint16_t bits16 = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
-                        if (it_v[r]) V[(cbase + i) * VP + v_pos(4 * t4 + k)] = bits16;
-                        else K[(4 * t4 + k) * KP + cbase + i] = bits16;
+                for (int i = 0; i < CPW; i += 2) {
+                    const float v0 = field_f32<BITS>(P.wd[r][k], i) * sk(k, i);
+                    const float v1 = (i + 1 < CPW) ? field_f32<BITS>(P.wd[r][k], i + 1) * sk(k, i + 1) : 0.0f;
+                    pw[i / 2] = pack_bf16x2(v0, v1);
+                }
+                if constexpr (CPW % 8 == 0) {
+#pragma unroll
+                    for (int i = 0; i < CPW / 2; i += 4)
+                        *reinterpret_cast<uint4 *>(dst + 2 * i) = make_uint4(pw[i], pw[i + 1], pw[i + 2], pw[i + 3]);
+                } else if constexpr (CPW % 4 == 0) {
+#pragma unroll
+                    for (int i = 0; i < CPW / 2; i += 2)
+                        *reinterpret_cast<uint2 *>(dst + 2 * i) = make_uint2(pw[i], pw[i + 1]);
+                } else if constexpr (CPW % 2 == 0) {
+#pragma unroll
+                    for (int i = 0; i < CPW / 2; ++i)
+                        if (2 * i < ncw) *reinterpret_cast<uint32_t *>(dst + 2 * i) = pw[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < CPW; ++i)
+                        if (i < ncw) dst[i] = (uint16_t)(pw[i / 2] >> (16 * (i & 1)));
+                }
+            }
+        }
+    };
+
+    // dequantize a prefetched tile starting at token n0 into LDS buffer `buf`
+    auto dequant = [&](int buf, const Pref &P, int n0) {
+#pragma unroll
+        for (int r = 0; r < IPT; ++r) {
+            if (!it_ok[r]) continue;
+            const int cbase = it_w[r] * CPW;
+            const int ncw = min(CPW, D - cbase);
+            if constexpr (SL) {
+                // scale rows in LDS: one per token (the tile's block unless split)
+                const float *base = sS + (it_v[r] ? AT_SL_MAXG * D : 0) + cbase;
+                if (!P.split) {
+                    float scl[CPW];
+#pragma unroll
+                    for (int i = 0; i < CPW; ++i) scl[i] = base[P.g * D + min(i, ncw - 1)];
+                    dequant_item(buf, P, r, [&](int, int i) { return scl[i]; });
+                } else {
+                    // a tile with a block boundary: token by token, scale rows
+                    // from LDS (K rows keep vector stores)
+                    uint16_t *K = Ks + buf * KBUF;
+                    uint16_t *V = Vt + buf * VBUF;
+                    const int t4 = it_t4[r];
+                    int g = P.g;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        g = group_of(off, g, min(n0 + 4 * t4 + k, L_kv - 1));
+                        const float *srow = base + g * D;
+                        if (it_v[r]) {
+#pragma unroll
+                            for (int i = 0; i < CPW; ++i) {
+                                if (i < ncw) {
+                                    const float v = field_f32<BITS>(P.wd[r][k], i) * srow[i];
+                                    V[(cbase + i) * VP + v_pos(4 * t4 + k)] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+                                }
+                            }
+                        } else {
+                            uint16_t *dst = K + (4 * t4 + k) * KP + cbase;
+#pragma unroll
+                            for (int i = 0; i < CPW; i += 2) {
+                                if (i < ncw) {
+                                    const float v0 = field_f32<BITS>(P.wd[r][k], i) * srow[i];
+                                    const float v1 = (i + 1 < CPW) ? field_f32<BITS>(P.wd[r][k], i + 1) * srow[min(i + 1, ncw - 1)] : 0.0f;
+                                    const uint32_t pw = pack_bf16x2(v0, v1);
+                                    if (i + 1 < ncw) *reinterpret_cast<uint32_t *>(dst + i) = pw;
+                                    else dst[i] = (uint16_t)(pw & 0xFFFFu);
+                                }
+                            }
+                        }
+                    }
+                }
+            } else if (!P.split) {
+                dequant_item(buf, P, r, [&](int, int i) { return P.sc[r][i]; });
+            } else {
+                // a tile with a block boundary (rare at this head_dim): per-token
+                // scale rows from memory, one token at a time to bound registers
+                uint16_t *K = Ks + buf * KBUF;
+                uint16_t *V = Vt + buf * VBUF;
+                const int t4 = it_t4[r];
+                int g = P.g;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    g = group_of(off, g, min(n0 + 4 * t4 + k, L_kv - 1));
+                    const float *srow = sbase[r] + g * D;
+#pragma unroll
+                    for (int i = 0; i < CPW; ++i) {
+                        if (i < ncw) {
+                            const float v = field_f32<BITS>(P.wd[r][k], i) * srow[i];
+                            const uint16_t bits16 = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+                            if (it_v[r]) V[(cbase + i) * VP + v_pos(4 * t4 + k)] = bits16;
+                            else K[(4 * t4 + k) * KP + cbase + i] = bits16;
+                        }
                     }
                 }
             }
@@ -367,22 +434,50 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         }
     };
 
-    // ---------------- pipeline: LDS-only barrier (global prefetches stay in flight)
+    // ---------------- pipeline: LDS-only barrier (global prefetches stay in
+    // flight). DEEP (head_dim 64, where registers allow): tile t is prefetched
+    // into set t % 2 two tiles before it is dequantized into LDS buffer t % 2;
+    // the loop is unrolled by two so that both register sets keep fixed names.
+    // Otherwise one set, one tile ahead.
     auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-    prefetch(0);
-    if (split_pref) dequant_slow(0, 0); else dequant_fast(0);
-    if (nt > 1) prefetch(AT_NT);
-    lds_barrier();
-    for (int jt = 0; jt + 1 < nt; ++jt) {
-        const int cur = jt & 1;
-        const int n0 = jt * AT_NT;
-        if (split_pref) dequant_slow(cur ^ 1, n0 + AT_NT);
-        else dequant_fast(cur ^ 1);
-        if (jt + 2 < nt) prefetch(n0 + 2 * AT_NT);
-        compute(cur, n0, false);
+    int jt = 0;
+    if constexpr (!DEEP) {
+        // one set: tile jt + 2 is prefetched while tile jt is computed
+        prefetch(P0, 0);
+        dequant(0, P0, 0);
+        if (nt > 1) prefetch(P0, AT_NT);
         lds_barrier();
+        for (; jt + 1 < nt; ++jt) {
+            const int cur = jt & 1;
+            const int n0 = jt * AT_NT;
+            dequant(cur ^ 1, P0, n0 + AT_NT);
+            if (jt + 2 < nt) prefetch(P0, n0 + 2 * AT_NT);
+            compute(cur, n0, false);
+            lds_barrier();
+        }
+    } else {
+    prefetch(P0, 0);
+    if (nt > 1) prefetch(P1, AT_NT);
+    dequant(0, P0, 0);
+    if (nt > 2) prefetch(P0, 2 * AT_NT);
+    lds_barrier();
+    while (jt + 1 < nt) {
+        // tile jt in buffer 0; tile jt + 1 in set 1
+        dequant(1, P1, (jt + 1) * AT_NT);
+        if (jt + 3 < nt) prefetch(P1, (jt + 3) * AT_NT);
+        compute(0, jt * AT_NT, false);
+        lds_barrier();
+        ++jt;
+        if (jt + 1 >= nt) break;
+        // tile jt in buffer 1; tile jt + 1 in set 0
+        dequant(0, P0, (jt + 1) * AT_NT);
+        if (jt + 3 < nt) prefetch(P0, (jt + 3) * AT_NT);
+        compute(1, jt * AT_NT, false);
+        lds_barrier();
+        ++jt;
     }
-    compute((nt - 1) & 1, (nt - 1) * AT_NT, true);
+    }
+    compute(jt & 1, jt * AT_NT, true);
 
     // ---------------- normalise and store
 #pragma unroll
@@ -420,8 +515,14 @@ template <int BITS, int D>
 static hipError_t launch_at(const AttnArgs &a, hipStream_t st) {
     const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H;
     const int64_t grid = (n_blocks + 7) / 8 * 8;
-    hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW>), dim3((unsigned)grid),
-                       dim3(64 * AT_CFG_NW), 0, st, a);
+    // head_dim 64 keeps up to AT_SL_MAXG blocks' scales in LDS (LDS still
+    // fits two work-groups per CU); otherwise scales stream with the words
+    if (D == 64 && a.G <= AT_SL_MAXG)
+        hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW, D == 64>), dim3((unsigned)grid),
+                           dim3(64 * AT_CFG_NW), 0, st, a);
+    else
+        hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW, false>), dim3((unsigned)grid),
+                           dim3(64 * AT_CFG_NW), 0, st, a);
     return hipGetLastError();
 }
 

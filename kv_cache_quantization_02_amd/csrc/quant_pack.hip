@@ -59,7 +59,24 @@ struct Unit {
     int row0, n;         // first row relative to x, rows
 };
 
-__device__ inline Unit unit_of(const QuantPackArgs &a, int64_t id) {
+// Packs: unit row where local block j + 1 starts (wave-uniform; past nb - 1
+// the entries never match).
+struct Bounds {
+    int b[QP_MAX_PACK - 1];
+};
+
+// Block offsets and unit starts live in LDS (copied once per work-group): a
+// lookup in the kernel-argument segment is a dependent scalar load that can
+// miss to memory at every step of a search. Values read are the same in all
+// lanes and are made wave-uniform.
+struct Tables {
+    const int32_t *off;   // [G + 1] block offsets relative to x
+    const int32_t *us;    // [G + 1] unit_start
+};
+
+__device__ inline int lds_uniform(const int32_t *p) { return __builtin_amdgcn_readfirstlane(*p); }
+
+__device__ inline Unit unit_of(const QuantPackArgs &a, const Tables &tb, int64_t id) {
     Unit U;
     U.id = id;
     U.bh = id / a.units_per_bh;
@@ -67,32 +84,40 @@ __device__ inline Unit unit_of(const QuantPackArgs &a, int64_t id) {
     int lo = 0, hi = a.G;                 // last g with unit_start[g] <= r_in
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (a.unit_start[mid] <= r_in) lo = mid; else hi = mid;
+        if (lds_uniform(tb.us + mid) <= r_in) lo = mid; else hi = mid;
     }
     const int T = a.chunk_rows;
-    const int len = a.off[lo + 1] - a.off[lo];
-    if (len > T) {
+    const int o_lo = lds_uniform(tb.off + lo), o_hi = lds_uniform(tb.off + lo + 1);
+    if (o_hi - o_lo > T) {
         U.g0 = lo; U.nb = 1;
-        U.c = r_in - a.unit_start[lo];
-        U.nc = (len + T - 1) / T;
-        U.row0 = a.off[lo] + U.c * T;
-        U.n = min(T, a.off[lo + 1] - U.row0);
+        U.c = r_in - lds_uniform(tb.us + lo);
+        U.nc = (o_hi - o_lo + T - 1) / T;
+        U.row0 = o_lo + U.c * T;
+        U.n = min(T, o_hi - U.row0);
     } else {
         int g0 = lo;
-        while (g0 > 0 && a.unit_start[g0 - 1] == r_in) --g0;
+        while (g0 > 0 && lds_uniform(tb.us + g0 - 1) == r_in) --g0;
         U.g0 = g0; U.nb = lo - g0 + 1;
         U.c = 0; U.nc = 1;
-        U.row0 = a.off[g0];
-        U.n = a.off[lo + 1] - a.off[g0];
+        U.row0 = lds_uniform(tb.off + g0);
+        U.n = o_hi - U.row0;
     }
     return U;
 }
 
+__device__ inline Bounds bounds_of(const Tables &tb, const Unit &U) {
+    Bounds B;
+#pragma unroll
+    for (int j = 0; j < QP_MAX_PACK - 1; ++j)
+        B.b[j] = j + 1 < U.nb ? lds_uniform(tb.off + U.g0 + 1 + j) - U.row0 : 0x7FFFFFFF;
+    return B;
+}
+
 // Local block (0 .. nb-1) of unit row r.
-__device__ inline int local_block(const QuantPackArgs &a, const Unit &U, int r) {
+__device__ inline int local_block(const Bounds &B, int r) {
     int lb = 0;
-    const int t = U.row0 + r;
-    for (int j = 1; j < U.nb; ++j) lb += t >= a.off[U.g0 + j] ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < QP_MAX_PACK - 1; ++j) lb += r >= B.b[j] ? 1 : 0;
     return lb;
 }
 
@@ -108,6 +133,7 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 __device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 struct Lane {
+    Tables tb;
     int chunk, rr, RP, lpr;
     uint32_t xoff;      // byte offset of this lane's 16 bytes within a row
     bool active;
@@ -157,7 +183,7 @@ __device__ inline void absmax_item(u16x2 (&m)[4], const uint4 &w) {
 // Per-(local block, channel) absmax of the unit in v, merged into sh_max as
 // fp32 bit patterns (non-negative floats order like their bit patterns; the
 // bf16 bit pattern of |x| is that of x with the sign bit cleared).
-__device__ inline void unit_absmax(const QuantPackArgs &a, const Unit &U, const uint4 (&v)[QP_ITEMS],
+__device__ inline void unit_absmax(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 (&v)[QP_ITEMS],
                                    const Lane &L, uint32_t *sh_max) {
     if (!L.active) return;
     u16x2 m[4];
@@ -174,7 +200,7 @@ __device__ inline void unit_absmax(const QuantPackArgs &a, const Unit &U, const 
     for (int k = 0; k < QP_ITEMS; ++k) {
         const int r = L.rr + k * L.RP;
         if (r < U.n) {
-            const int lb = local_block(a, U, r);          // non-decreasing in k
+            const int lb = local_block(B, r);          // non-decreasing in k
             if (lb != cur) {
                 flush_max(sh_max, cur, L.chunk, m);
 #pragma unroll
@@ -226,25 +252,27 @@ __device__ inline bool load_sy(const float *sh_s, const float *sh_y, int slot, i
 
 // Fields of item k of unit U. SIMPLE: one block whose scales all allow the
 // division-free quotient, scales already in s8/y8. Otherwise the item's block
-// is looked up (packs) and each channel picks its quotient.
+// is looked up (packs), and unless the scales of every lane of the wave allow
+// the division-free quotient, each channel picks its quotient.
 template <bool SIMPLE>
-__device__ inline void item_codes(const QuantPackArgs &a, const Unit &U, const uint4 &w, const Lane &L, int r,
-                                  int slot, const float *sh_s, const float *sh_y, float (&s8)[8], float (&y8)[8],
-                                  int &cur, uint32_t (&f)[8]) {
+__device__ inline void item_codes(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 &w,
+                                  const Lane &L, int r, int slot, const float *sh_s, const float *sh_y,
+                                  float (&s8)[8], float (&y8)[8], int &cur, bool &fast, uint32_t (&f)[8]) {
     if (SIMPLE) {
         codes8<true>(w, s8, y8, f);
     } else {
-        const int lb = U.nb > 1 ? local_block(a, U, r) : slot;
-        if (lb != cur) { load_sy(sh_s, sh_y, lb, L.chunk, s8, y8); cur = lb; }
-        codes8<false>(w, s8, y8, f);
+        const int lb = U.nb > 1 ? local_block(B, r) : slot;
+        if (lb != cur) { fast = load_sy(sh_s, sh_y, lb, L.chunk, s8, y8); cur = lb; }
+        if (__all(fast)) codes8<true>(w, s8, y8, f);
+        else codes8<false>(w, s8, y8, f);
     }
 }
 
 // Words of unit U formed in registers, written to LDS as sh_w[plane * wp + row].
 template <int BITS, bool SIMPLE>
-__device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const uint4 (&v)[QP_ITEMS],
+__device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 (&v)[QP_ITEMS],
                                    const Lane &L, int slot, const float *sh_s, const float *sh_y,
-                                   float (&s8)[8], float (&y8)[8], int cur, uint32_t *sh_w, int wp) {
+                                   float (&s8)[8], float (&y8)[8], int cur, bool fast, uint32_t *sh_w, int wp) {
     constexpr uint32_t MASK = (1u << BITS) - 1u;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
@@ -255,9 +283,9 @@ __device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const 
         for (int j = 0; j < 8; ++j) f[j] = 0;
         if (SIMPLE) {
             // rows past n repeat row n-1; their fields are discarded below
-            item_codes<true>(a, U, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, f);
+            item_codes<true>(a, U, B, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, fast, f);
         } else if (live) {
-            item_codes<false>(a, U, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, f);
+            item_codes<false>(a, U, B, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, fast, f);
         }
         if constexpr (BITS == 4) {
             uint32_t w = 0;
@@ -287,16 +315,16 @@ __device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const 
 }
 
 template <int BITS, bool SIMPLE>
-__device__ inline void stage_codes(const QuantPackArgs &a, const Unit &U, const uint4 (&v)[QP_ITEMS],
+__device__ inline void stage_codes(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 (&v)[QP_ITEMS],
                                    const Lane &L, int slot, const float *sh_s, const float *sh_y,
-                                   float (&s8)[8], float (&y8)[8], int cur, uint8_t *sh_codes, int pitch) {
+                                   float (&s8)[8], float (&y8)[8], int cur, bool fast, uint8_t *sh_codes, int pitch) {
     constexpr uint32_t MASK = (1u << BITS) - 1u;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
         const int r = L.rr + k * L.RP;
         if (L.active && r < U.n) {
             uint32_t f[8];
-            item_codes<SIMPLE>(a, U, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, f);
+            item_codes<SIMPLE>(a, U, B, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, fast, f);
             uint8_t *dst = sh_codes + r * pitch + 8 * L.chunk;
             *reinterpret_cast<uint32_t *>(dst) =
                 (f[0] & MASK) | ((f[1] & MASK) << 8) | ((f[2] & MASK) << 16) | ((f[3] & MASK) << 24);
@@ -310,7 +338,7 @@ __device__ inline void stage_codes(const QuantPackArgs &a, const Unit &U, const 
 // (packs: slot = local block). Ends with a barrier, after which LDS may be
 // rewritten.
 template <int BITS>
-__device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, const uint4 (&v)[QP_ITEMS],
+__device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 (&v)[QP_ITEMS],
                                      const Lane &L, int slot, const float *sh_s, const float *sh_y,
                                      uint8_t *sh_codes) {
     constexpr int CPW = 32 / BITS;
@@ -337,8 +365,8 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
         // wave (chunks x rows) then write distinct banks.
         uint32_t *sh_w = reinterpret_cast<uint32_t *>(sh_codes);
         const int wp = a.chunk_rows + 64 / L.lpr;
-        if (simple) stage_words<BITS, true>(a, U, v, L, slot, sh_s, sh_y, s8, y8, cur, sh_w, wp);
-        else stage_words<BITS, false>(a, U, v, L, slot, sh_s, sh_y, s8, y8, cur, sh_w, wp);
+        if (simple) stage_words<BITS, true>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
+        else stage_words<BITS, false>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
         lds_barrier();
         wait_loads();
         for (int i = tid; i < a.W * span; i += QP_THREADS) {
@@ -351,8 +379,8 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
 
     // ---- fields -> LDS code rows -> words, one plane at a time
     const int pitch = D >= 64 ? D + 4 : D;
-    if (simple) stage_codes<BITS, true>(a, U, v, L, slot, sh_s, sh_y, s8, y8, cur, sh_codes, pitch);
-    else stage_codes<BITS, false>(a, U, v, L, slot, sh_s, sh_y, s8, y8, cur, sh_codes, pitch);
+    if (simple) stage_codes<BITS, true>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_codes, pitch);
+    else stage_codes<BITS, false>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_codes, pitch);
     lds_barrier();
     wait_loads();
     for (int i = tid; i < a.W * span; i += QP_THREADS) {
@@ -434,10 +462,18 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
     __shared__ __attribute__((aligned(16))) float sh_s[(QP_MAX_PACK + 2) * 256];
     __shared__ __attribute__((aligned(16))) float sh_y[(QP_MAX_PACK + 2) * 256];
     __shared__ __attribute__((aligned(16))) uint8_t sh_codes[QP_UNIT_ELEMS + 4 * 512];
+    __shared__ int32_t sh_off[VARQ_MAX_GROUPS_DEV + 1];
+    __shared__ int32_t sh_us[VARQ_MAX_GROUPS_DEV + 1];
 
     const int tid = threadIdx.x;
     const int D = a.D;
+    for (int i = tid; i <= a.G; i += QP_THREADS) {
+        sh_off[i] = a.off[i];
+        sh_us[i] = a.unit_start[i];
+    }
     Lane L;
+    L.tb.off = sh_off;
+    L.tb.us = sh_us;
     L.lpr = D >> 3;
     L.RP = QP_THREADS / L.lpr;
     L.chunk = tid % L.lpr;
@@ -464,10 +500,13 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
     // loads (loads complete in issue order) and stay in flight while the
     // ready units are quantized.
     uint4 X[QP_ITEMS], Z[QP_ITEMS], D1[QP_ITEMS], D2[QP_ITEMS];
+    Bounds BX1;                               // deferred units are single blocks: no bounds
+#pragma unroll
+    for (int j = 0; j < QP_MAX_PACK - 1; ++j) BX1.b[j] = 0x7FFFFFFF;
     Unit UX, UZ, U1 = {}, U2 = {};
     bool has1 = false, has2 = false;          // D1: deferred one unit ago; D2: two units ago
     int64_t u = blockIdx.x;
-    if (u < a.n_units) { UZ = unit_of(a, u); load_unit(a, UZ, Z, L); }
+    if (u < a.n_units) { UZ = unit_of(a, L.tb, u); load_unit(a, UZ, Z, L); }
     while (u < a.n_units) {
         UX = UZ;
         copy_regs(X, Z);
@@ -479,7 +518,8 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
         uint64_t v2 = 0;
         if (has2 && tid < D) v2 = load_slot(fin2);
 
-        unit_absmax(a, UX, X, L, sh_max);
+        const Bounds BX = bounds_of(L.tb, UX);
+        unit_absmax(a, UX, BX, X, L, sh_max);
         lds_barrier();
         const bool splitX = UX.nc > 1;
         if (tid < D) {
@@ -509,11 +549,11 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
             }
             if (has2) put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin2, v2, epoch, status));
         }
-        if (u < a.n_units) { UZ = unit_of(a, u); load_unit(a, UZ, Z, L); }
+        if (u < a.n_units) { UZ = unit_of(a, L.tb, u); load_unit(a, UZ, Z, L); }
         lds_barrier();
-        if (has2) quantize_unit<BITS>(a, U2, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
-        if (last1) quantize_unit<BITS>(a, U1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
-        if (!splitX) quantize_unit<BITS>(a, UX, X, L, 0, sh_s, sh_y, sh_codes);
+        if (has2) quantize_unit<BITS>(a, U2, BX1, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
+        if (last1) quantize_unit<BITS>(a, U1, BX1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
+        if (!splitX) quantize_unit<BITS>(a, UX, BX, X, L, 0, sh_s, sh_y, sh_codes);
         // advance the deferral pipeline
         has2 = has1 && !last1;
         if (has2) { U2 = U1; copy_regs(D2, D1); }
@@ -531,7 +571,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
             *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, tid, m);
         }
         lds_barrier();
-        quantize_unit<BITS>(a, U1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
+        quantize_unit<BITS>(a, U1, BX1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
         has1 = false;
     }
     if (has2) {
@@ -540,7 +580,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
             put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin2, load_slot(fin2), epoch, status));
         }
         lds_barrier();
-        quantize_unit<BITS>(a, U2, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
+        quantize_unit<BITS>(a, U2, BX1, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
     }
     if (has1) {
         if (tid < D) {
@@ -548,7 +588,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
             put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin1, load_slot(fin1), epoch, status));
         }
         lds_barrier();
-        quantize_unit<BITS>(a, U1, D1, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
+        quantize_unit<BITS>(a, U1, BX1, D1, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
     }
 
     // ---- the last work-group to finish advances the epoch for the next launch
