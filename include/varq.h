@@ -13,7 +13,8 @@
  *
  * Conventions for every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
- *    frees them and keeps no reference after the call returns.
+ *    frees them and keeps no reference after the call returns. The only memory
+ *    the library allocates is varq_quantize_pack's scratch (described there).
  *  - `group_offsets` is a HOST array of G+1 int32 prefix offsets
  *    0 = o_0 < o_1 < ... < o_G: block g covers tokens [o_g, o_{g+1}).
  *    G <= VARQ_MAX_GROUPS per call.
@@ -91,7 +92,17 @@ int varq_cache_bytes(int B, int H, int head_dim, int64_t L_cap, int64_t G_cap, i
  *               written, nothing else. 4-byte aligned.
  *  D            head_dim: a multiple of 8, 8 <= D <= 256.
  * Errors: VARQ_EBITS, VARQ_EINVAL, VARQ_EALIGN, VARQ_ECAPACITY
- * (tok_start+L_in > L_cap or group_start+G_in > G_cap), VARQ_ELAUNCH.
+ * (tok_start+L_in > L_cap or group_start+G_in > G_cap), VARQ_EUNSUPPORTED (a
+ * block of more 16384-element chunks than resident work-groups, or a token
+ * stride or cache length beyond 32-bit byte offsets), VARQ_ELAUNCH.
+ * Scratch: when some block is longer than one work-group's 16384 elements
+ * (16384 / D token rows), its chunks exchange per-channel maxima through
+ * device scratch that the library owns per (device, stream): 12 bytes of
+ * launch state plus 8 bytes per (chunk, channel) and per (block, channel),
+ * grown on demand with hipMalloc (after synchronizing that stream) and kept
+ * until the process ends. Such launches are cooperative (every work-group
+ * resident). Calls on one stream are ordered; calls on different streams use
+ * different scratch.
  * Deterministic: the output does not depend on launch order or timing.
  */
 int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
