@@ -37,6 +37,8 @@
 // < x, and the iterations before it in that work-group end by induction. So
 // P(x) happens, a contradiction; every gather and wait then ends. Spins are
 // nevertheless bounded and report a timeout through a status word.
+#include <mutex>
+
 #include "varq_device.h"
 
 namespace varq {
@@ -132,8 +134,12 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // does not also wait for these stores to be acknowledged.
 __device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Thread (chunk, rr) holds channels [8 chunk, 8 chunk + 8) of the unit's rows
+// [8 rr, 8 rr + 8): consecutive rows, so a thread's rows rarely span two
+// blocks of a pack.
 struct Lane {
     Tables tb;
+    int D;              // head_dim = LDS slot stride
     int chunk, rr, RP, lpr;
     uint32_t xoff;      // byte offset of this lane's 16 bytes within a row
     bool active;
@@ -150,7 +156,7 @@ __device__ inline void load_unit(const QuantPackArgs &a, const Unit &U, uint4 (&
     const uint32_t row_bytes = (uint32_t)a.sx_l * 2u;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
-        const int r = min(L.rr + k * L.RP, U.n - 1);
+        const int r = min(L.rr * QP_ITEMS + k, U.n - 1);
         v[k] = *reinterpret_cast<const uint4 *>(ubase + (uint32_t)r * row_bytes + L.xoff);
     }
 }
@@ -162,8 +168,8 @@ __device__ inline uint32_t *word_at(const QuantPackArgs &a, const Unit &U, int p
     return reinterpret_cast<uint32_t *>(base + (uint32_t)(p * (uint32_t)a.L_cap + r) * 4u);
 }
 
-__device__ inline void flush_max(uint32_t *sh_max, int lb, int chunk, const u16x2 (&m)[4]) {
-    uint32_t *dst = sh_max + lb * 256 + 8 * chunk;
+__device__ inline void flush_max(uint32_t *sh_max, int lb, const Lane &L, const u16x2 (&m)[4]) {
+    uint32_t *dst = sh_max + lb * L.D + 8 * L.chunk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t w = __builtin_bit_cast(uint32_t, m[j]);
@@ -192,17 +198,17 @@ __device__ inline void unit_absmax(const QuantPackArgs &a, const Unit &U, const 
     if (U.nb == 1) {
 #pragma unroll
         for (int k = 0; k < QP_ITEMS; ++k) absmax_item(m, v[k]);      // rows past n repeat row n-1
-        flush_max(sh_max, 0, L.chunk, m);
+        flush_max(sh_max, 0, L, m);
         return;
     }
     int cur = 0;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
-        const int r = L.rr + k * L.RP;
+        const int r = L.rr * QP_ITEMS + k;
         if (r < U.n) {
             const int lb = local_block(B, r);          // non-decreasing in k
             if (lb != cur) {
-                flush_max(sh_max, cur, L.chunk, m);
+                flush_max(sh_max, cur, L, m);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) m[j] = u16x2{0, 0};
                 cur = lb;
@@ -210,7 +216,7 @@ __device__ inline void unit_absmax(const QuantPackArgs &a, const Unit &U, const 
             absmax_item(m, v[k]);
         }
     }
-    flush_max(sh_max, cur, L.chunk, m);
+    flush_max(sh_max, cur, L, m);
 }
 
 // b-bit two's complement fields (low bits of each word, higher bits garbage)
@@ -235,10 +241,10 @@ __device__ inline void codes8(const uint4 &w, const float (&s8)[8], const float 
     }
 }
 
-__device__ inline bool load_sy(const float *sh_s, const float *sh_y, int slot, int chunk, float (&s8)[8],
+__device__ inline bool load_sy(const float *sh_s, const float *sh_y, int slot, const Lane &L, float (&s8)[8],
                                float (&y8)[8]) {
-    const float4 *ps = reinterpret_cast<const float4 *>(sh_s + slot * 256 + 8 * chunk);
-    const float4 *py = reinterpret_cast<const float4 *>(sh_y + slot * 256 + 8 * chunk);
+    const float4 *ps = reinterpret_cast<const float4 *>(sh_s + slot * L.D + 8 * L.chunk);
+    const float4 *py = reinterpret_cast<const float4 *>(sh_y + slot * L.D + 8 * L.chunk);
     const float4 s0 = ps[0], s1 = ps[1], y0 = py[0], y1 = py[1];
     s8[0] = s0.x; s8[1] = s0.y; s8[2] = s0.z; s8[3] = s0.w;
     s8[4] = s1.x; s8[5] = s1.y; s8[6] = s1.z; s8[7] = s1.w;
@@ -262,7 +268,7 @@ __device__ inline void item_codes(const QuantPackArgs &a, const Unit &U, const B
         codes8<true>(w, s8, y8, f);
     } else {
         const int lb = U.nb > 1 ? local_block(B, r) : slot;
-        if (lb != cur) { fast = load_sy(sh_s, sh_y, lb, L.chunk, s8, y8); cur = lb; }
+        if (lb != cur) { fast = load_sy(sh_s, sh_y, lb, L, s8, y8); cur = lb; }
         if (__all(fast)) codes8<true>(w, s8, y8, f);
         else codes8<false>(w, s8, y8, f);
     }
@@ -276,7 +282,7 @@ __device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const 
     constexpr uint32_t MASK = (1u << BITS) - 1u;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
-        const int r = L.rr + k * L.RP;
+        const int r = L.rr * QP_ITEMS + k;
         const bool live = L.active && r < U.n;
         uint32_t f[8];
 #pragma unroll
@@ -321,7 +327,7 @@ __device__ inline void stage_codes(const QuantPackArgs &a, const Unit &U, const 
     constexpr uint32_t MASK = (1u << BITS) - 1u;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
-        const int r = L.rr + k * L.RP;
+        const int r = L.rr * QP_ITEMS + k;
         if (L.active && r < U.n) {
             uint32_t f[8];
             item_codes<SIMPLE>(a, U, B, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, fast, f);
@@ -353,7 +359,7 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
     // wave's channels allows the division-free quotient
     float s8[8], y8[8];
     bool fast = true;
-    if (U.nb == 1 && L.active) fast = load_sy(sh_s, sh_y, slot, L.chunk, s8, y8);
+    if (U.nb == 1 && L.active) fast = load_sy(sh_s, sh_y, slot, L, s8, y8);
     const bool simple = U.nb == 1 && __all(fast);
     const int cur = U.nb == 1 ? slot : -1;
 
@@ -361,10 +367,10 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
     const int span = 1 << tshift;
     if (direct) {
         // words -> LDS planes -> global, consecutive lanes on consecutive
-        // tokens of a plane. Plane pitch T + 64/lanes-per-row: the lanes of a
-        // wave (chunks x rows) then write distinct banks.
+        // tokens of a plane. Odd plane pitch T + 1: the lanes of a wave (chunks
+        // x rows 8 apart) then write distinct banks.
         uint32_t *sh_w = reinterpret_cast<uint32_t *>(sh_codes);
-        const int wp = a.chunk_rows + 64 / L.lpr;
+        const int wp = a.chunk_rows + 1;
         if (simple) stage_words<BITS, true>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
         else stage_words<BITS, false>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
         lds_barrier();
@@ -438,11 +444,11 @@ __device__ inline float gather_partials(const uint64_t *p, int n, int D, float m
 
 // Scale and reciprocal of maximum m into LDS slot `slot` (thread = channel).
 template <int BITS>
-__device__ inline float put_scale(float *sh_s, float *sh_y, int slot, int tid, float m) {
+__device__ inline float put_scale(float *sh_s, float *sh_y, int slot, int D, int tid, float m) {
     constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
     const float s = m / QMAX;                                       // IEEE fp32 division
-    sh_s[slot * 256 + tid] = s;
-    sh_y[slot * 256 + tid] = recip_for_codes(s);
+    sh_s[slot * D + tid] = s;
+    sh_y[slot * D + tid] = recip_for_codes(s);
     return s;
 }
 
@@ -456,14 +462,19 @@ __device__ inline void copy_regs(uint4 (&dst)[N], const uint4 (&src)[N]) {
     for (int k = 0; k < N; ++k) dst[k] = src[k];
 }
 
-template <int BITS>
-__global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPackArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t sh_max[QP_MAX_PACK * 256];
-    __shared__ __attribute__((aligned(16))) float sh_s[(QP_MAX_PACK + 2) * 256];
-    __shared__ __attribute__((aligned(16))) float sh_y[(QP_MAX_PACK + 2) * 256];
-    __shared__ __attribute__((aligned(16))) uint8_t sh_codes[QP_UNIT_ELEMS + 4 * 512];
-    __shared__ int32_t sh_off[VARQ_MAX_GROUPS_DEV + 1];
-    __shared__ int32_t sh_us[VARQ_MAX_GROUPS_DEV + 1];
+// SPLIT: some block of this launch spans several units (exchange through
+// scratch, cooperative launch). Otherwise every unit holds whole blocks and a
+// work-group just quantizes its units one after another. LDS is sized by the
+// host for this launch (regions at byte offsets a.lds_*).
+template <int BITS, bool SPLIT>
+__global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t qp_lds[];
+    uint32_t *sh_max = reinterpret_cast<uint32_t *>(qp_lds + a.lds_max);   // [QP_MAX_PACK][D]
+    float *sh_s = reinterpret_cast<float *>(qp_lds + a.lds_s);             // [QP_MAX_PACK + 2][D]
+    float *sh_y = reinterpret_cast<float *>(qp_lds + a.lds_y);             // [QP_MAX_PACK + 2][D]
+    uint8_t *sh_codes = qp_lds + a.lds_codes;                              // code rows or word planes
+    int32_t *sh_off = reinterpret_cast<int32_t *>(qp_lds + a.lds_off);     // [G + 1]
+    int32_t *sh_us = reinterpret_cast<int32_t *>(qp_lds + a.lds_us);       // [G + 1]
 
     const int tid = threadIdx.x;
     const int D = a.D;
@@ -474,6 +485,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
     Lane L;
     L.tb.off = sh_off;
     L.tb.us = sh_us;
+    L.D = D;
     L.lpr = D >> 3;
     L.RP = QP_THREADS / L.lpr;
     L.chunk = tid % L.lpr;
@@ -481,15 +493,34 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
     L.active = L.rr < L.RP;
     L.xoff = (uint32_t)(8 * L.chunk) * 2u;
     const int64_t step = gridDim.x;
-    const bool split = a.part != nullptr;     // some block spans several chunks
-    uint32_t *status = a.sync + 2;
+    for (int i = tid; i < QP_MAX_PACK * D; i += QP_THREADS) sh_max[i] = 0;
 
-    uint32_t epoch = 0;
-    if (split) {
-        epoch = __hip_atomic_load(a.sync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        if (epoch == 0) epoch = 1;
+    if constexpr (!SPLIT) {
+        lds_barrier();
+        for (int64_t u = blockIdx.x; u < a.n_units; u += step) {
+            const Unit U = unit_of(a, L.tb, u);
+            uint4 X[QP_ITEMS];
+            load_unit(a, U, X, L);
+            const Bounds B = bounds_of(L.tb, U);
+            unit_absmax(a, U, B, X, L, sh_max);
+            lds_barrier();
+            // scales of the unit's blocks, (block, channel) pairs over all threads
+            float *scl = scale_ptr(a, U, 0);
+            for (int i = tid; i < U.nb * D; i += QP_THREADS) {
+                const float m = u2f(sh_max[i]);
+                sh_max[i] = 0;
+                const int lb = i / D, c = i - lb * D;
+                scl[i] = put_scale<BITS>(sh_s, sh_y, lb, D, c, m);
+            }
+            lds_barrier();
+            quantize_unit<BITS>(a, U, B, X, L, 0, sh_s, sh_y, sh_codes);
+        }
+        return;
     }
-    for (int i = tid; i < QP_MAX_PACK * 256; i += QP_THREADS) sh_max[i] = 0;
+
+    uint32_t *status = a.sync + 2;
+    uint32_t epoch = __hip_atomic_load(a.sync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    if (epoch == 0) epoch = 1;
     lds_barrier();
 
     // Per unit X: absmax; a chunk of a split block publishes its partial and
@@ -535,19 +566,19 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
                 for (int lb = 0; lb < UX.nb; ++lb) {
                     float m = m0;
                     if (lb > 0) {
-                        m = u2f(sh_max[lb * 256 + tid]);
-                        sh_max[lb * 256 + tid] = 0;
+                        m = u2f(sh_max[lb * D + tid]);
+                        sh_max[lb * D + tid] = 0;
                     }
-                    scl[(int64_t)lb * D] = put_scale<BITS>(sh_s, sh_y, lb, tid, m);
+                    scl[(int64_t)lb * D] = put_scale<BITS>(sh_s, sh_y, lb, D, tid, m);
                 }
             }
             if (last1) {
                 const float m = gather_partials(a.part + (U1.id - U1.c) * D + tid, U1.nc, D, 0.0f, epoch, status);
                 __hip_atomic_store(a.fin + (U1.bh * a.G + U1.g0) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-                *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, tid, m);
+                *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, D, tid, m);
             }
-            if (has2) put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin2, v2, epoch, status));
+            if (has2) put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin2, v2, epoch, status));
         }
         if (u < a.n_units) { UZ = unit_of(a, L.tb, u); load_unit(a, UZ, Z, L); }
         lds_barrier();
@@ -568,7 +599,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
             const float m = gather_partials(a.part + (U1.id - U1.c) * D + tid, U1.nc, D, 0.0f, epoch, status);
             __hip_atomic_store(a.fin + (U1.bh * a.G + U1.g0) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-            *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, tid, m);
+            *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, D, tid, m);
         }
         lds_barrier();
         quantize_unit<BITS>(a, U1, BX1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
@@ -577,7 +608,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
     if (has2) {
         if (tid < D) {
             const uint64_t *fin2 = a.fin + (U2.bh * a.G + U2.g0) * D + tid;
-            put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin2, load_slot(fin2), epoch, status));
+            put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin2, load_slot(fin2), epoch, status));
         }
         lds_barrier();
         quantize_unit<BITS>(a, U2, BX1, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
@@ -585,14 +616,14 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
     if (has1) {
         if (tid < D) {
             const uint64_t *fin1 = a.fin + (U1.bh * a.G + U1.g0) * D + tid;
-            put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, tid, slot_max(fin1, load_slot(fin1), epoch, status));
+            put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin1, load_slot(fin1), epoch, status));
         }
         lds_barrier();
         quantize_unit<BITS>(a, U1, BX1, D1, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
     }
 
     // ---- the last work-group to finish advances the epoch for the next launch
-    if (split && tid == 0) {
+    if (tid == 0) {
         const uint32_t done = __hip_atomic_fetch_add(a.sync + 1, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
             __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -602,21 +633,22 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_onepass(const QuantPack
 }
 
 template <int BITS>
-static hipError_t launch_qp(const QuantPackArgs &a, int grid, bool cooperative, hipStream_t st) {
-    if (!cooperative) {
-        hipLaunchKernelGGL(quant_pack_onepass<BITS>, dim3(grid), dim3(QP_THREADS), 0, st, a);
+static hipError_t launch_qp(const QuantPackArgs &a, int grid, bool split, hipStream_t st) {
+    if (!split) {
+        hipLaunchKernelGGL((quant_pack_kernel<BITS, false>), dim3(grid), dim3(QP_THREADS), a.lds_bytes, st, a);
         return hipGetLastError();
     }
     void *args[] = {const_cast<QuantPackArgs *>(&a)};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&quant_pack_onepass<BITS>),
-                                      dim3(grid), dim3(QP_THREADS), args, 0, st);
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&quant_pack_kernel<BITS, true>),
+                                      dim3(grid), dim3(QP_THREADS), args, (unsigned)a.lds_bytes, st);
 }
 
 template <int BITS>
-static int qp_resident_blocks() {
+static int qp_resident_blocks(int lds_bytes) {
     int per_cu = 0, cus = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_pack_onepass<BITS>, QP_THREADS, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_pack_kernel<BITS, true>, QP_THREADS,
+                                                     (size_t)lds_bytes) != hipSuccess)
         return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     return per_cu * cus;
@@ -625,35 +657,41 @@ static int qp_resident_blocks() {
 int quant_pack_unit_elems() { return QP_UNIT_ELEMS; }
 int quant_pack_max_pack() { return QP_MAX_PACK; }
 
-int quant_pack_resident_blocks(int bits) {
-    constexpr int kMaxDev = 64;
-    static int cached[kMaxDev][9];   // resident work-groups per (device, bits); 0 = not yet queried
+// Work-groups of the split kernel that fit the device at once, for this LDS
+// size (cached per device, bit width and LDS size).
+int quant_pack_resident_blocks(int bits, int lds_bytes) {
+    struct Entry { int dev, bits, lds, n; };
+    static Entry cache[64];
+    static int used = 0;
+    static std::mutex mu;
     int dev = 0;
     if (bits < 2 || bits > 8 || hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev < kMaxDev && cached[dev][bits] > 0) return cached[dev][bits];
+    std::lock_guard<std::mutex> lk(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].dev == dev && cache[i].bits == bits && cache[i].lds == lds_bytes) return cache[i].n;
     int r = 0;
     switch (bits) {
-        case 2: r = qp_resident_blocks<2>(); break;
-        case 3: r = qp_resident_blocks<3>(); break;
-        case 4: r = qp_resident_blocks<4>(); break;
-        case 5: r = qp_resident_blocks<5>(); break;
-        case 6: r = qp_resident_blocks<6>(); break;
-        case 7: r = qp_resident_blocks<7>(); break;
-        case 8: r = qp_resident_blocks<8>(); break;
+        case 2: r = qp_resident_blocks<2>(lds_bytes); break;
+        case 3: r = qp_resident_blocks<3>(lds_bytes); break;
+        case 4: r = qp_resident_blocks<4>(lds_bytes); break;
+        case 5: r = qp_resident_blocks<5>(lds_bytes); break;
+        case 6: r = qp_resident_blocks<6>(lds_bytes); break;
+        case 7: r = qp_resident_blocks<7>(lds_bytes); break;
+        case 8: r = qp_resident_blocks<8>(lds_bytes); break;
     }
-    if (dev < kMaxDev) cached[dev][bits] = r;
+    if (r > 0 && used < 64) cache[used++] = Entry{dev, bits, lds_bytes, r};
     return r;
 }
 
-hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, int grid, bool cooperative, hipStream_t st) {
+hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, int grid, bool split, hipStream_t st) {
     switch (bits) {
-        case 2: return launch_qp<2>(a, grid, cooperative, st);
-        case 3: return launch_qp<3>(a, grid, cooperative, st);
-        case 4: return launch_qp<4>(a, grid, cooperative, st);
-        case 5: return launch_qp<5>(a, grid, cooperative, st);
-        case 6: return launch_qp<6>(a, grid, cooperative, st);
-        case 7: return launch_qp<7>(a, grid, cooperative, st);
-        case 8: return launch_qp<8>(a, grid, cooperative, st);
+        case 2: return launch_qp<2>(a, grid, split, st);
+        case 3: return launch_qp<3>(a, grid, split, st);
+        case 4: return launch_qp<4>(a, grid, split, st);
+        case 5: return launch_qp<5>(a, grid, split, st);
+        case 6: return launch_qp<6>(a, grid, split, st);
+        case 7: return launch_qp<7>(a, grid, split, st);
+        case 8: return launch_qp<8>(a, grid, split, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -17,8 +17,8 @@
 #include "varq_device.h"
 
 namespace varq {
-hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, int grid, bool cooperative, hipStream_t st);
-int quant_pack_resident_blocks(int bits);
+hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, int grid, bool split, hipStream_t st);
+int quant_pack_resident_blocks(int bits, int lds_bytes);
 int quant_pack_max_pack();
 hipError_t launch_unpack_dequant(const UnpackArgs &a, int bits, hipStream_t st);
 hipError_t launch_packed_attention(const AttnArgs &a, int D, int bits, hipStream_t st);
@@ -220,11 +220,30 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
     a.unit_start[G_in] = units;
     a.units_per_bh = units;
     a.n_units = (int64_t)B * H * units;
-    const int resident = varq::quant_pack_resident_blocks(bits);
-    if (resident <= 0) return fail(VARQ_ELAUNCH, "quantize_pack: cannot query the device occupancy");
-    const int grid = (int)std::min<int64_t>(a.n_units, resident);
     const bool split = max_nc > 1;
+
+    // LDS regions (bytes, 16-aligned): block maxima [max_pack][D], scales and
+    // reciprocals [max_pack + 2][D], the staging area for words or code rows
+    // (words at 2, 4, 7, 8 bits, and 2 bits only with an even number of 16-byte
+    // chunks per row), then the block-offset and unit-start tables.
+    {
+        auto up16 = [](int64_t v) { return (int)((v + 15) / 16 * 16); };
+        const bool direct = bits == 4 || bits == 7 || bits == 8 || (bits == 2 && lpr % 2 == 0);
+        const int64_t stage = direct ? (int64_t)a.W * (T + 1) * 4 : (int64_t)T * (D >= 64 ? D + 4 : D);
+        int o = 0;
+        a.lds_max = o;   o += up16((int64_t)max_pack * D * 4);
+        a.lds_s = o;     o += up16((int64_t)(max_pack + 2) * D * 4);
+        a.lds_y = o;     o += up16((int64_t)(max_pack + 2) * D * 4);
+        a.lds_codes = o; o += up16(stage);
+        a.lds_off = o;   o += up16((int64_t)(G_in + 1) * 4);
+        a.lds_us = o;    o += up16((int64_t)(G_in + 1) * 4);
+        a.lds_bytes = o;
+    }
+    int grid = 0;
     if (split) {
+        const int resident = varq::quant_pack_resident_blocks(bits, a.lds_bytes);
+        if (resident <= 0) return fail(VARQ_ELAUNCH, "quantize_pack: cannot query the device occupancy");
+        grid = (int)std::min<int64_t>(a.n_units, resident);
         // chunks of one block wait for each other: all work-groups must be
         // resident and no block may have more chunks than there are work-groups
         if (max_nc > grid)
@@ -238,6 +257,9 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
         a.sync = sync;
         a.part = slots;
         a.fin = slots + (size_t)a.n_units * D;
+    } else {
+        // whole blocks only: one work-group per unit
+        grid = (int)std::min<int64_t>(a.n_units, (int64_t)1 << 30);
     }
     return launch_status(varq::launch_quant_pack(a, bits, grid, split, static_cast<hipStream_t>(stream)),
                          "quantize_pack");

@@ -33,6 +33,7 @@ struct QuantPackArgs {
     int64_t n_units;
     int B, H, D, W, G;
     int chunk_rows, rows_log2, units_per_bh;
+    int lds_max, lds_s, lds_y, lds_codes, lds_off, lds_us, lds_bytes;   // dynamic LDS layout (bytes)
     int32_t off[VARQ_MAX_GROUPS_DEV + 1];          // token offsets relative to x
     int32_t unit_start[VARQ_MAX_GROUPS_DEV + 1];
 };

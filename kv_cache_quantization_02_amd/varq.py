@@ -12,6 +12,7 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -169,7 +170,7 @@ def packed_attention(q, packed_k, scales_k, packed_v, scales_v, group_offsets, b
     B, Lq, H, D = q.shape
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
-    softmax_scale = float(torch.tensor(softmax_scale, dtype=torch.float32))
+    softmax_scale = float(np.float32(softmax_scale))      # the fp32 value the kernel uses
     if out is None:
         out = torch.empty(B, Lq, H, D, dtype=torch.bfloat16, device=q.device)
     _need(out, torch.bfloat16, "out")
