@@ -160,6 +160,50 @@ def cpu_baseline(wl, bits, budget_s):
                       f"{dt:.1f} s; numpy/BLAS threads <= {threads}"}
 
 
+# ---------------------------------------------------------------- unfused baseline
+
+def unfused_compare(varq, torch, wl, bits, launches, off, q, pk, sk, pv, sv, args, fused_ms):
+    """The attention calls of one step done the unfused way: unpack+dequant of
+    K and V into bf16 workspaces, then plain bf16 attention. Timed with HIP
+    events per call (same stream), outside the main timed region."""
+    calls = [st for st in launches if st[0] != "qp"]
+    if not calls:
+        return None
+    B, H, D = wl.B, wl.H, wl.D
+    L_max = max(st[3] for st in calls)
+    kd = torch.empty(B, H, L_max, D, dtype=torch.bfloat16, device=q.device)
+    vd = torch.empty_like(kd)
+    out = torch.empty_like(q)
+
+    def one(st):
+        _, q0, ql, L_kv, g1 = st
+        # contiguous [B, H, L_kv, D] views at the start of the workspaces
+        kw = kd.view(-1)[:B * H * L_kv * D].view(B, H, L_kv, D)
+        vw = vd.view(-1)[:B * H * L_kv * D].view(B, H, L_kv, D)
+        varq.unpack_dequant(pk, sk, off[:g1 + 1], bits, out=kw)
+        varq.unpack_dequant(pv, sv, off[:g1 + 1], bits, out=vw)
+        varq.bf16_attention(q, kw, vw, out=out)
+
+    for _ in range(max(1, args.warmup)):
+        for st in calls:
+            one(st)
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(len(calls) * args.steps)]
+    i = 0
+    for _ in range(args.steps):
+        for st in calls:
+            pairs[i][0].record()
+            one(st)
+            pairs[i][1].record()
+            i += 1
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+    return {"path": "unpack_dequant(K), unpack_dequant(V) into bf16, then bf16_attention",
+            "avg_ms_per_call": round(ms, 5), "fused_avg_ms_per_call": round(fused_ms, 5),
+            "fused_speedup": round(ms / fused_ms, 3) if fused_ms else None}
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -206,7 +250,25 @@ def main():
             at_f.append(attn_flops(B, H, D, ql, L_kv))
             step_bytes += b1
 
-    events = {"qp": [], "attn": []}
+    # one event pair per launch of every timed step, created before timing
+    n_qp_launches = sum(2 for st in launches if st[0] == "qp")
+    n_at_launches = sum(1 for st in launches if st[0] != "qp")
+
+    def event_pairs(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    events = {"qp": event_pairs(n_qp_launches * args.steps), "attn": event_pairs(n_at_launches * args.steps)}
+    used = {"qp": 0, "attn": 0}
+
+    def timed(kind, record, fn):
+        if not record:
+            fn()
+            return
+        e0, e1 = events[kind][used[kind]]
+        used[kind] += 1
+        e0.record()
+        fn()
+        e1.record()
 
     def step(record):
         for st in launches:
@@ -214,24 +276,11 @@ def main():
                 _, t0, t1, g0, g1 = st
                 rel = [o - t0 for o in off[g0:g1 + 1]]
                 for x, p, s in ((k, pk, sk), (v, pv, sv)):
-                    if record:
-                        e0 = torch.cuda.Event(enable_timing=True)
-                        e1 = torch.cuda.Event(enable_timing=True)
-                        e0.record()
-                    varq.quantize_pack(x[:, t0:t1], rel, bits, p, s, tok_start=t0, group_start=g0)
-                    if record:
-                        e1.record()
-                        events["qp"].append((e0, e1))
+                    timed("qp", record, lambda: varq.quantize_pack(x[:, t0:t1], rel, bits, p, s,
+                                                                   tok_start=t0, group_start=g0))
             else:
                 _, q0, ql, L_kv, g1 = st
-                if record:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                varq.packed_attention(q, pk, sk, pv, sv, off[:g1 + 1], bits, out=out)
-                if record:
-                    e1.record()
-                    events["attn"].append((e0, e1))
+                timed("attn", record, lambda: varq.packed_attention(q, pk, sk, pv, sv, off[:g1 + 1], bits, out=out))
 
     for _ in range(args.warmup):
         step(False)
@@ -244,8 +293,8 @@ def main():
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps
 
-    qp_ms = [a.elapsed_time(b) for a, b in events["qp"]]
-    at_ms = [a.elapsed_time(b) for a, b in events["attn"]]
+    qp_ms = [a.elapsed_time(b) for a, b in events["qp"][:used["qp"]]]
+    at_ms = [a.elapsed_time(b) for a, b in events["attn"][:used["attn"]]]
     n_qp_per_step = max(1, len(qp_b))
     n_at_per_step = max(1, len(at_b))
     qp_avg_ms = sum(qp_ms) / len(qp_ms) if qp_ms else 0.0
@@ -282,6 +331,8 @@ def main():
                 "frac": round(at_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": (tr["fetch_bytes"] + tr["write_bytes"]) if tr else None}
 
+    unfused = unfused_compare(varq, torch, wl, bits, launches, off, q, pk, sk, pv, sv, args, at_avg_ms)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, bits, args.cpu_budget_s)
@@ -308,6 +359,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "unfused": unfused,
     }
     print(json.dumps(line), flush=True)
 

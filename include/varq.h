@@ -158,6 +158,31 @@ int varq_unpack_dequant(const int32_t *packed, const float *scales,
                         const int32_t *group_offsets, int G, int bits,
                         void *out, void *stream);
 
+/*
+ * Plain bf16 attention over dense K and V: the unfused baseline that the
+ * fused varq_packed_attention is measured against (README "Deployment
+ * Results": fusing packed-KV load, unpack and dequant into attention; the
+ * unfused path first writes the dequantized cache with varq_unpack_dequant).
+ * Same result definition as varq_packed_attention with K^, V^ given directly:
+ *   O[b,i,h,:] = softmax_j(Q[b,i,h,:] . K[b,h,j,:] * softmax_scale) V[b,h,j,:],
+ * j in [0, L_kv), no mask; logits, softmax and accumulation in fp32; bf16 out.
+ *  q            bf16 [B, Lq, H, D] at strides (sq_b, sq_l, sq_h); 16-byte aligned,
+ *               strides multiples of 8.
+ *  k, v         bf16 [B, H, L_rows, D], contiguous (varq_unpack_dequant's output
+ *               layout), 16-byte aligned; L_kv <= L_rows.
+ *  D            64 or 128.
+ *  out          bf16 [B, Lq, H, D] at strides (so_b, so_l, so_h); 8-byte aligned,
+ *               strides multiples of 4. Must not overlap q, k or v.
+ * Errors: VARQ_EINVAL, VARQ_EALIGN, VARQ_ECAPACITY (L_kv > L_rows),
+ * VARQ_EUNSUPPORTED (D not 64/128), VARQ_ELAUNCH.
+ */
+int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
+                        int B, int H, int D, int64_t Lq,
+                        const void *k, const void *v, int64_t L_rows, int64_t L_kv,
+                        float softmax_scale,
+                        void *out, int64_t so_b, int64_t so_l, int64_t so_h,
+                        void *stream);
+
 /* Text of the last error reported to the calling thread ("" if none). */
 const char *varq_last_error(void);
 

@@ -1,7 +1,8 @@
 """MI355X (gfx950) implementation of VAR-Q's packed KV-cache hot path.
 
 The compute lives in libvarq.so (C ABI in include/varq.h): quantize+pack,
-unpack+dequant and packed-KV attention as hand-written HIP kernels. The module
+unpack+dequant and packed-KV attention as hand-written HIP kernels, plus a
+plain bf16 attention over dense K/V for the unfused comparison. The module
 `varq` is a thin ctypes binding over it.
 """
 
@@ -9,6 +10,7 @@ from . import varq  # noqa: F401
 from .varq import (  # noqa: F401
     VarqError,
     alloc_cache,
+    bf16_attention,
     cache_bytes,
     codes_per_word,
     packed_attention,

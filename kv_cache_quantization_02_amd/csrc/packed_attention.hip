@@ -67,9 +67,13 @@ __device__ inline void scale_acc16(floatx16 &o, float alpha) {
 #undef VARQ_SCALE_ONE
 }
 
+// BITS = 16 (DENSE): K and V are plain bf16 [B, H, rows, D] (the unfused
+// baseline: unpack+dequant first, then this kernel); items are then 4 tokens
+// x 8 channels of K or V.
 template <int BITS, int D, int QB, int NW>
 struct AttnTile {
-    static constexpr int CPW = 32 / BITS;
+    static constexpr bool DENSE = BITS == 16;
+    static constexpr int CPW = DENSE ? 8 : 32 / BITS;
     static constexpr int W = (D + CPW - 1) / CPW;
     static constexpr int KP = D + 8;          // K row pitch (bf16)
     static constexpr int VP = AT_NT + 8;      // V^T row pitch (bf16)
@@ -77,6 +81,7 @@ struct AttnTile {
     static constexpr int QW = 32 * QB;        // queries per wave
     static constexpr int QT = NW * QW;        // queries per work-group
     static constexpr int NITEMS = 32 * W;     // 16W K items then 16W V items (4 tokens each)
+    static constexpr int WORDS = DENSE ? 16 : 4;   // 32-bit words an item loads
     static constexpr int IPT = (NITEMS + THREADS - 1) / THREADS;
 };
 
@@ -94,13 +99,13 @@ __device__ inline int v_pos(int tok) {
 template <int BITS, int D, int QB, int NW, bool SL>
 __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a) {
     using T = AttnTile<BITS, D, QB, NW>;
+    constexpr bool DENSE = T::DENSE;
     constexpr int CPW = T::CPW, W = T::W, KP = T::KP, VP = T::VP;
     constexpr int THREADS = T::THREADS, QW = T::QW, QT = T::QT;
     constexpr int NITEMS = T::NITEMS, IPT = T::IPT;
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
     constexpr int KBUF = AT_NT * KP, VBUF = D * VP;
-    constexpr bool DEEP = false;
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
@@ -177,22 +182,26 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         it_w[r] = isV ? (j >> 4) : (j % W);
         it_t4[r] = isV ? (j & 15) : (j / W);
         if (!it_ok[r]) { it_w[r] = 0; it_t4[r] = 0; it_v[r] = false; }
-        plane[r] = (it_v[r] ? a.pv : a.pk) + ((int64_t)bh * W + it_w[r]) * a.L_cap + 4 * it_t4[r];
-        sbase[r] = (it_v[r] ? a.sv : a.sk) + (int64_t)bh * a.G_cap * D + it_w[r] * CPW;
+        if constexpr (DENSE)
+            plane[r] = reinterpret_cast<const uint32_t *>((it_v[r] ? a.vd : a.kd) + (int64_t)bh * a.L_cap * D +
+                                                          it_w[r] * CPW);
+        else
+            plane[r] = (it_v[r] ? a.pv : a.pk) + ((int64_t)bh * W + it_w[r]) * a.L_cap + 4 * it_t4[r];
+        sbase[r] = DENSE ? nullptr : (it_v[r] ? a.sv : a.sk) + (int64_t)bh * a.G_cap * D + it_w[r] * CPW;
     }
 
     // Prefetched tile: words per item and, when the tile lies in one block and
     // scales are not in LDS, that block's scales for the item's channels. Two
     // sets alternate so that a tile's loads are issued two tiles ahead.
     struct Pref {
-        uint32_t wd[IPT][4];
+        uint32_t wd[IPT][T::WORDS];
         float sc[IPT][CPW];
         int g;        // block of the tile's first token
         bool split;   // the tile contains a block boundary
     };
-    Pref P0, P1;
-    P0.g = P1.g = 0;
-    P0.split = P1.split = false;
+    Pref P0;
+    P0.g = 0;
+    P0.split = false;
     int g_run = 0;    // search hint: block of the last prefetched tile
 
     __syncthreads();   // off[] (and scales in LDS) ready
@@ -200,6 +209,21 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     // words of tile n0 (always in bounds: t + 4 <= L_cap) and, for a tile inside
     // one block, that block's scales
     auto prefetch = [&](Pref &P, int n0) {
+        if constexpr (DENSE) {
+            // 4 rows of 8 channels per item; rows past L_kv re-read the last
+            // row (masked in compute): the dense buffer has exactly L_cap rows
+#pragma unroll
+            for (int r = 0; r < IPT; ++r) {
+                if (!it_ok[r]) continue;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int t = min(n0 + 4 * it_t4[r] + k, L_kv - 1);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(plane[r] + (int64_t)t * (D / 2));
+                    P.wd[r][4 * k] = v.x; P.wd[r][4 * k + 1] = v.y; P.wd[r][4 * k + 2] = v.z; P.wd[r][4 * k + 3] = v.w;
+                }
+            }
+            return;
+        }
         g_run = group_of(off, g_run, n0);
         P.g = g_run;
         P.split = off[g_run + 1] < min(n0 + AT_NT, L_kv);
@@ -283,6 +307,33 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
 
     // dequantize a prefetched tile starting at token n0 into LDS buffer `buf`
     auto dequant = [&](int buf, const Pref &P, int n0) {
+        if constexpr (DENSE) {
+            // bf16 rows as they are: K row-major, V transposed
+            uint16_t *K = Ks + buf * KBUF;
+            uint16_t *V = Vt + buf * VBUF;
+#pragma unroll
+            for (int r = 0; r < IPT; ++r) {
+                if (!it_ok[r]) continue;
+                const int c8 = it_w[r] * 8, t4 = it_t4[r];
+                if (!it_v[r]) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        *reinterpret_cast<uint4 *>(K + (4 * t4 + k) * KP + c8) =
+                            make_uint4(P.wd[r][4 * k], P.wd[r][4 * k + 1], P.wd[r][4 * k + 2], P.wd[r][4 * k + 3]);
+                } else {
+                    const int p0 = v_pos(4 * t4);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        // channel c8 + i of tokens 0..3: half i & 1 of word i / 2 of each row
+                        const int sh = 16 * (i & 1);
+                        const uint32_t e0 = (P.wd[r][i / 2] >> sh) & 0xFFFFu, e1 = (P.wd[r][4 + i / 2] >> sh) & 0xFFFFu;
+                        const uint32_t e2 = (P.wd[r][8 + i / 2] >> sh) & 0xFFFFu, e3 = (P.wd[r][12 + i / 2] >> sh) & 0xFFFFu;
+                        *reinterpret_cast<uint2 *>(V + (c8 + i) * VP + p0) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < IPT; ++r) {
             if (!it_ok[r]) continue;
@@ -435,47 +486,21 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     };
 
     // ---------------- pipeline: LDS-only barrier (global prefetches stay in
-    // flight). DEEP (head_dim 64, where registers allow): tile t is prefetched
-    // into set t % 2 two tiles before it is dequantized into LDS buffer t % 2;
-    // the loop is unrolled by two so that both register sets keep fixed names.
-    // Otherwise one set, one tile ahead.
+    // flight); tile jt + 2 is prefetched while tile jt is computed and tile
+    // jt + 1 dequantized into the other LDS buffer.
     auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
     int jt = 0;
-    if constexpr (!DEEP) {
-        // one set: tile jt + 2 is prefetched while tile jt is computed
-        prefetch(P0, 0);
-        dequant(0, P0, 0);
-        if (nt > 1) prefetch(P0, AT_NT);
-        lds_barrier();
-        for (; jt + 1 < nt; ++jt) {
-            const int cur = jt & 1;
-            const int n0 = jt * AT_NT;
-            dequant(cur ^ 1, P0, n0 + AT_NT);
-            if (jt + 2 < nt) prefetch(P0, n0 + 2 * AT_NT);
-            compute(cur, n0, false);
-            lds_barrier();
-        }
-    } else {
     prefetch(P0, 0);
-    if (nt > 1) prefetch(P1, AT_NT);
     dequant(0, P0, 0);
-    if (nt > 2) prefetch(P0, 2 * AT_NT);
+    if (nt > 1) prefetch(P0, AT_NT);
     lds_barrier();
-    while (jt + 1 < nt) {
-        // tile jt in buffer 0; tile jt + 1 in set 1
-        dequant(1, P1, (jt + 1) * AT_NT);
-        if (jt + 3 < nt) prefetch(P1, (jt + 3) * AT_NT);
-        compute(0, jt * AT_NT, false);
+    for (; jt + 1 < nt; ++jt) {
+        const int cur = jt & 1;
+        const int n0 = jt * AT_NT;
+        dequant(cur ^ 1, P0, n0 + AT_NT);
+        if (jt + 2 < nt) prefetch(P0, n0 + 2 * AT_NT);
+        compute(cur, n0, false);
         lds_barrier();
-        ++jt;
-        if (jt + 1 >= nt) break;
-        // tile jt in buffer 1; tile jt + 1 in set 0
-        dequant(0, P0, (jt + 1) * AT_NT);
-        if (jt + 3 < nt) prefetch(P0, (jt + 3) * AT_NT);
-        compute(1, jt * AT_NT, false);
-        lds_barrier();
-        ++jt;
-    }
     }
     compute(jt & 1, jt * AT_NT, true);
 
@@ -541,6 +566,22 @@ static hipError_t launch_at_bits(const AttnArgs &a, int bits, hipStream_t st) {
 }
 
 int attention_q_tile() { return 32 * AT_CFG_QB * AT_CFG_NW; }
+
+// Dense bf16 K/V (the unfused baseline): the same pipeline and compute, with
+// tiles staged from bf16 rows instead of dequantized from packed words.
+hipError_t launch_dense_attention(const AttnArgs &a, int D, hipStream_t st) {
+    const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H;
+    const int64_t grid = (n_blocks + 7) / 8 * 8;
+    if (D == 64)
+        hipLaunchKernelGGL((packed_attention_v5<16, 64, AT_CFG_QB, AT_CFG_NW, false>), dim3((unsigned)grid),
+                           dim3(64 * AT_CFG_NW), 0, st, a);
+    else if (D == 128)
+        hipLaunchKernelGGL((packed_attention_v5<16, 128, AT_CFG_QB, AT_CFG_NW, false>), dim3((unsigned)grid),
+                           dim3(64 * AT_CFG_NW), 0, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_packed_attention(const AttnArgs &a, int D, int bits, hipStream_t st) {
     if (D == 64) return launch_at_bits<64>(a, bits, st);

@@ -22,6 +22,7 @@ int quant_pack_resident_blocks(int bits, int lds_bytes);
 int quant_pack_max_pack();
 hipError_t launch_unpack_dequant(const UnpackArgs &a, int bits, hipStream_t st);
 hipError_t launch_packed_attention(const AttnArgs &a, int D, int bits, hipStream_t st);
+hipError_t launch_dense_attention(const AttnArgs &a, int D, hipStream_t st);
 int attention_q_tile();
 }  // namespace varq
 
@@ -350,6 +351,51 @@ int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
     for (int g = 0; g <= G; ++g) a.off[g] = group_offsets[g];
     return launch_status(varq::launch_packed_attention(a, D, bits, static_cast<hipStream_t>(stream)),
                          "packed_attention");
+}
+
+int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
+                        int B, int H, int D, int64_t Lq,
+                        const void *k, const void *v, int64_t L_rows, int64_t L_kv,
+                        float softmax_scale,
+                        void *out, int64_t so_b, int64_t so_l, int64_t so_h,
+                        void *stream) {
+    if (B < 1 || H < 1) return fail(VARQ_EINVAL, "bf16_attention: B=%d H=%d must be >= 1", B, H);
+    if (D != 64 && D != 128)
+        return fail(VARQ_EUNSUPPORTED, "bf16_attention: head_dim %d not implemented (64 or 128)", D);
+    if (Lq < 0) return fail(VARQ_EINVAL, "bf16_attention: Lq=%lld < 0", (long long)Lq);
+    if (Lq == 0) return ok();
+    if (L_kv < 1) return fail(VARQ_EINVAL, "bf16_attention: the window is empty (L_kv=%lld)", (long long)L_kv);
+    if (L_kv > L_rows)
+        return fail(VARQ_ECAPACITY, "bf16_attention: L_kv=%lld exceeds the %lld rows of k and v",
+                    (long long)L_kv, (long long)L_rows);
+    if (!q || !k || !v || !out) return fail(VARQ_EINVAL, "bf16_attention: NULL tensor pointer");
+    if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f)
+        return fail(VARQ_EINVAL, "bf16_attention: softmax_scale must be finite and > 0");
+    if (!aligned(q, 16) || sq_b % 8 || sq_l % 8 || sq_h % 8)
+        return fail(VARQ_EALIGN, "bf16_attention: q must be 16-byte aligned with strides that are multiples of 8");
+    if (!aligned(out, 8) || so_b % 4 || so_l % 4 || so_h % 4)
+        return fail(VARQ_EALIGN, "bf16_attention: out must be 8-byte aligned with strides that are multiples of 4");
+    if (!aligned(k, 16) || !aligned(v, 16))
+        return fail(VARQ_EALIGN, "bf16_attention: k and v must be 16-byte aligned");
+    const int qtile = varq::attention_q_tile();
+    const int64_t n_qtiles = (Lq + qtile - 1) / qtile;
+    if (n_qtiles * B * H >= (1LL << 31) - 8) return fail(VARQ_EINVAL, "bf16_attention: grid too large");
+
+    varq::AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = static_cast<const uint16_t *>(q);
+    a.sq_b = sq_b; a.sq_l = sq_l; a.sq_h = sq_h;
+    a.kd = static_cast<const uint16_t *>(k);
+    a.vd = static_cast<const uint16_t *>(v);
+    a.out = static_cast<uint16_t *>(out);
+    a.so_b = so_b; a.so_l = so_l; a.so_h = so_h;
+    a.L_cap = L_rows; a.G_cap = 1; a.L_kv = L_kv; a.Lq = Lq;
+    a.B = B; a.H = H; a.W = D / 8; a.G = 1;
+    a.n_qtiles = (int)n_qtiles;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    a.off[0] = 0;
+    a.off[1] = (int32_t)L_kv;
+    return launch_status(varq::launch_dense_attention(a, D, static_cast<hipStream_t>(stream)), "bf16_attention");
 }
 
 const char *varq_last_error(void) { return g_last_error.c_str(); }

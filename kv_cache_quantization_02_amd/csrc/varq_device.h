@@ -52,6 +52,7 @@ struct AttnArgs {
     int64_t sq_b, sq_l, sq_h;
     const uint32_t *pk, *pv;    // [B, H, W, L_cap]
     const float *sk, *sv;       // [B, H, G_cap, D]
+    const uint16_t *kd, *vd;    // dense bf16 [B, H, L_cap, D] (unfused baseline; pk/pv unused)
     uint16_t *out;              // bf16 [B, Lq, H, D]
     int64_t so_b, so_l, so_h;
     int64_t L_cap, G_cap, L_kv, Lq;

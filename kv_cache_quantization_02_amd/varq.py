@@ -43,6 +43,8 @@ _SIGNATURES = {
                                      _f32, _vp, _i64, _i64, _i64, _vp]),
     "varq_unpack_dequant": (_i32, [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32p, _i32, _i32,
                                    _vp, _vp]),
+    "varq_bf16_attention": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _vp, _vp, _i64, _i64,
+                                   _f32, _vp, _i64, _i64, _i64, _vp]),
     "varq_last_error": (ctypes.c_char_p, []),
     "varq_version": (ctypes.c_char_p, []),
 }
@@ -182,6 +184,34 @@ def packed_attention(q, packed_k, scales_k, packed_v, scales_v, group_offsets, b
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), B, H, D, Lq,
         packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
         packed_k.shape[3], scales_k.shape[2], L_kv, off, G, bits, softmax_scale,
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2), _stream(stream, q.device)))
+    return out
+
+
+def bf16_attention(q, k, v, L_kv=None, softmax_scale=None, out=None, stream=None):
+    """Unfused baseline: q bf16 [B, Lq, H, D] attends to dense bf16 k, v
+    [B, H, L_rows, D] (e.g. unpack_dequant's output) over rows [0, L_kv) ->
+    out bf16 [B, Lq, H, D]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+    if q.dim() != 4 or q.stride(3) != 1:
+        raise ValueError("q must be [B, Lq, H, D] with channel stride 1")
+    if not k.is_contiguous() or not v.is_contiguous() or k.shape != v.shape:
+        raise ValueError("k and v must be contiguous [B, H, L_rows, D] of one shape")
+    B, Lq, H, D = q.shape
+    L_rows = k.shape[2]
+    L_kv = L_rows if L_kv is None else int(L_kv)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    softmax_scale = float(np.float32(softmax_scale))
+    if out is None:
+        out = torch.empty(B, Lq, H, D, dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out")
+    if out.stride(3) != 1:
+        raise ValueError("out must have channel stride 1")
+    _check(lib().varq_bf16_attention(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), B, H, D, Lq,
+        k.data_ptr(), v.data_ptr(), L_rows, L_kv, softmax_scale,
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2), _stream(stream, q.device)))
     return out
 

@@ -129,6 +129,21 @@ def test_packed_attention_validation(V):
     assert _attn(V, sv=0) == -1
 
 
+def test_bf16_attention_validation(V):
+    f = V.lib().varq_bf16_attention
+
+    def call(D=64, Lq=16, q=0x10000, k=0x20000, v=0x30000, L_rows=64, L_kv=64, scale=0.125, out=0x40000,
+             sq=(64 * 16 * 64, 16 * 64, 64), so=(64 * 16 * 64, 16 * 64, 64)):
+        return f(q, sq[0], sq[1], sq[2], 1, 16, D, Lq, k, v, L_rows, L_kv, scale, out, so[0], so[1], so[2], None)
+
+    assert call(D=96) == -6
+    assert call(Lq=0) == 0
+    assert call(L_kv=0) == -1 and call(scale=0.0) == -1 and call(v=0) == -1
+    assert call(L_kv=65) == -4
+    assert call(k=0x20008) == -3 and call(q=0x10002) == -3 and call(sq=(8, 8, 4)) == -3
+    assert call(out=0x40002) == -3
+
+
 def test_unpack_dequant_validation(V):
     f = V.lib().varq_unpack_dequant
     off = (ctypes.c_int32 * 3)(0, 4, 10)

@@ -395,3 +395,45 @@ def test_attention_deterministic(V):
     o2 = V.packed_attention(q, *caches, off, 4)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------- unfused baseline
+
+def test_bf16_attention_matches_oracle(V):
+    """Dense bf16 attention (the unfused path's second step) against the fp64
+    oracle on random bf16 K/V: several 64-token tiles and a ragged tail."""
+    _say("[dense attention vs oracle]")
+    g = torch.Generator().manual_seed(5)
+    for (B, H, D, Lq, L) in [(2, 3, 64, 300, 261), (1, 2, 128, 257, 200)]:
+        q = torch.randn(B, Lq, H, D, generator=g).to(torch.bfloat16)
+        k = torch.randn(B, H, L, D, generator=g).to(torch.bfloat16)
+        v = (torch.randn(B, H, L, D, generator=g) * 3).to(torch.bfloat16)
+        out = V.bf16_attention(q.to(DEV), k.to(DEV), v.to(DEV))
+        torch.cuda.synchronize()
+        _, C, ob = O.attention_fp64(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                    O.default_softmax_scale(D))
+        _assert_attn(_gpu_rows(out), ob, C, tag=f"dense D={D}")
+
+
+@pytest.mark.parametrize("name,bits,pairs", [("var_d30", 4, None), ("infinity_8b", 2, 24)])
+def test_unfused_equals_fused(V, name, bits, pairs):
+    """unpack_dequant into a bf16 workspace followed by bf16_attention gives the
+    same bf16 output, bit for bit, as the fused packed attention: both see the
+    same dequantized values and run the same tile arithmetic."""
+    wl = WORKLOADS[name]
+    _say(f"[unfused == fused {name} bits={bits}]")
+    k, v, q = workload_inputs(wl, seed=0, device=DEV)
+    B = wl.B if pairs is None else 1
+    k, v, q = k[:B], v[:B], q[:B]
+    off = list(wl.offsets)
+    pk, sk = _gpu_qp(V, k, off, bits)
+    pv, sv = _gpu_qp(V, v, off, bits)
+    qs, ql, lkv = wl.calls[-1]
+    goff = off[:off.index(lkv) + 1]
+    qq = q[:, :ql]
+    fused = V.packed_attention(qq, pk, sk, pv, sv, goff, bits)
+    kd = V.unpack_dequant(pk, sk, goff, bits)
+    vd = V.unpack_dequant(pv, sv, goff, bits)
+    unfused = V.bf16_attention(qq, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), unfused.view(torch.int16))
