@@ -222,6 +222,32 @@ def test_incremental_append_equals_one_shot(V):
     assert torch.equal(one, inc) and torch.equal(s_one, s_inc)
 
 
+def test_block_overwrite_in_place(V):
+    """Chunk overwrite: re-quantizing one block at its token and block offsets
+    replaces exactly that block's words and scales; the cache then equals a
+    one-shot quantization of the edited sequence (blocks are independent)."""
+    wl = WORKLOADS["longlive"]
+    _say("[qp block overwrite]")
+    k, _, _ = workload_inputs(wl, seed=0, device=DEV, with_v=False)
+    k = k[:1]
+    off = list(wl.offsets)
+    bits = 3
+    pk, sk = _gpu_qp(V, k, off, bits)
+    g = 17                                   # overwrite frame block 17 with new content
+    t0, t1 = off[g], off[g + 1]
+    new = (torch.randn(1, t1 - t0, wl.H, wl.D, generator=torch.Generator().manual_seed(9)) * 4)
+    new = new.to(torch.bfloat16).to(DEV)
+    V.quantize_pack(new, [0, t1 - t0], bits, pk, sk, tok_start=t0, group_start=g)
+    edited = k.clone()
+    edited[:, t0:t1] = new
+    ref_pk, ref_sk = _gpu_qp(V, edited, off, bits)
+    torch.cuda.synchronize()
+    assert torch.equal(pk, ref_pk) and torch.equal(sk, ref_sk)
+    w, s = O.quantize_pack(new.float().cpu().numpy(), [0, t1 - t0], bits)
+    assert np.array_equal(_words(pk[:, :, :, t0:t1]), w)
+    assert np.array_equal(_f32bits(sk[:, :, g:g + 1]), s.view(np.uint32))
+
+
 # ---------------------------------------------------------------- unpack+dequant
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
