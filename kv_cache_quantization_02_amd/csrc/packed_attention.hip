@@ -348,37 +348,30 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
                     for (int i = 0; i < CPW; ++i) scl[i] = base[P.g * D + min(i, ncw - 1)];
                     dequant_item(buf, P, r, [&](int, int i) { return scl[i]; });
                 } else {
-                    // a tile with a block boundary: token by token, scale rows
-                    // from LDS (K rows keep vector stores)
-                    uint16_t *K = Ks + buf * KBUF;
-                    uint16_t *V = Vt + buf * VBUF;
-                    const int t4 = it_t4[r];
+                    // a tile with a block boundary: each token takes the scale
+                    // row of its own block; the same vector path for every item,
+                    // so no lane of a wave waits on a slower one
+                    const int t0 = n0 + 4 * it_t4[r];
                     int g = P.g;
+                    if constexpr (CPW <= 8) {
+                        // up to 32 scales: held in registers
+                        float scl[4][CPW];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        g = group_of(off, g, min(n0 + 4 * t4 + k, L_kv - 1));
-                        const float *srow = base + g * D;
-                        if (it_v[r]) {
+                        for (int k = 0; k < 4; ++k) {
+                            g = group_of(off, g, min(t0 + k, L_kv - 1));
 #pragma unroll
-                            for (int i = 0; i < CPW; ++i) {
-                                if (i < ncw) {
-                                    const float v = field_f32<BITS>(P.wd[r][k], i) * srow[i];
-                                    V[(cbase + i) * VP + v_pos(4 * t4 + k)] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
-                                }
-                            }
-                        } else {
-                            uint16_t *dst = K + (4 * t4 + k) * KP + cbase;
-#pragma unroll
-                            for (int i = 0; i < CPW; i += 2) {
-                                if (i < ncw) {
-                                    const float v0 = field_f32<BITS>(P.wd[r][k], i) * srow[i];
-                                    const float v1 = (i + 1 < CPW) ? field_f32<BITS>(P.wd[r][k], i + 1) * srow[min(i + 1, ncw - 1)] : 0.0f;
-                                    const uint32_t pw = pack_bf16x2(v0, v1);
-                                    if (i + 1 < ncw) *reinterpret_cast<uint32_t *>(dst + i) = pw;
-                                    else dst[i] = (uint16_t)(pw & 0xFFFFu);
-                                }
-                            }
+                            for (int i = 0; i < CPW; ++i) scl[k][i] = base[g * D + min(i, ncw - 1)];
                         }
+                        dequant_item(buf, P, r, [&](int k, int i) { return scl[k][i]; });
+                    } else {
+                        // wider words: scales read where used, to bound registers
+                        const float *row[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            g = group_of(off, g, min(t0 + k, L_kv - 1));
+                            row[k] = base + g * D;
+                        }
+                        dequant_item(buf, P, r, [&](int k, int i) { return row[k][min(i, ncw - 1)]; });
                     }
                 }
             } else if (!P.split) {
@@ -409,45 +402,58 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     };
 
     const float c = a.scale_log2;
+    // at head_dim 64 the 16 registers of early scores would cost the second
+    // resident workgroup per CU
+    constexpr bool EARLY_S = (D >= 128);
 
     // one 64-token tile from LDS buffer `buf`
     auto compute = [&](int buf, int n0, bool masked) {
         const uint16_t *Kb = Ks + buf * KBUF + lr * KP + 8 * hf;
         const uint16_t *Vb = Vt + buf * VBUF + lr * VP + 8 * hf;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            floatx16 s[QB];
+        floatx16 s[2][QB];
+        auto scores = [&](int tb) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[qb][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) s[tb][qb][r] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 const bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4 *>(Kb + 32 * tb * KP + 16 * ks));
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][ks], s[qb], 0, 0, 0);
+                    s[tb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][ks], s[tb][qb], 0, 0, 0);
             }
+        };
+        // EARLY_S: scores of both 32-token halves first, so that the matrix
+        // core works on the second half while the first half's softmax runs on
+        // the vector ALUs (costs 16 registers per query block)
+        if constexpr (EARLY_S) { scores(0); scores(1); }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            if constexpr (!EARLY_S) scores(tb);
             if (masked) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int tok = n0 + 32 * tb + 8 * (r >> 2) + 4 * hf + (r & 3);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb)
-                        if (tok >= L_kv) s[qb][r] = -INFINITY;
+                        if (tok >= L_kv) s[tb][qb][r] = -INFINITY;
                 }
             }
             bf16x8 pop[QB][2];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                float mx = fmaxf(s[qb][0], s[qb][1]);
+                // scores are finite or -inf (masked), never NaN: the NaN-propagating
+                // maximum takes two new values per instruction and needs no quieting
+                float mx = __builtin_elementwise_maximum(s[tb][qb][0], s[tb][qb][1]);
 #pragma unroll
-                for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r], s[qb][r + 1]));
+                for (int r = 2; r < 16; r += 2)
+                    mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[tb][qb][r], s[tb][qb][r + 1]));
                 const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
                                                                  __builtin_bit_cast(uint32_t, mx), false, false);
                 // the swap returns the values of this lane's pair (lanes i and i^32)
-                mx = fmaxf(mx, fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
-                                     __builtin_bit_cast(float, (uint32_t)sw[1])));
+                mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)sw[0]),
+                                                                                     __builtin_bit_cast(float, (uint32_t)sw[1])));
                 const float mt = mx * c;
                 if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + AT_RESCALE_SLACK) != 0) {
                     const float m_new = fmaxf(m_run[qb], mt);
@@ -463,8 +469,8 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
                     uint32_t u[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hh + 2 * e], c, mneg));
-                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hh + 2 * e + 1], c, mneg));
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][8 * hh + 2 * e], c, mneg));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][8 * hh + 2 * e + 1], c, mneg));
                         u[e] = pack_bf16x2(p0, p1);
                         l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[e]), ones_bf16x2(),
                                                                     l_run[qb], false);
@@ -497,9 +503,12 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     for (; jt + 1 < nt; ++jt) {
         const int cur = jt & 1;
         const int n0 = jt * AT_NT;
+        // with EARLY_S the next tile's dequantization follows this tile's
+        // compute and overlaps its last matrix ops; otherwise it goes first
+        if constexpr (EARLY_S) compute(cur, n0, false);
         dequant(cur ^ 1, P0, n0 + AT_NT);
         if (jt + 2 < nt) prefetch(P0, n0 + 2 * AT_NT);
-        compute(cur, n0, false);
+        if constexpr (!EARLY_S) compute(cur, n0, false);
         lds_barrier();
     }
     compute(jt & 1, jt * AT_NT, true);
