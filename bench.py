@@ -285,13 +285,20 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    # timed region: K steps, wall clock between two synchronizations
+    # timed region: K steps, wall clock between two synchronizations. No events
+    # here: each timing event leaves the GPU idle for a few microseconds, which
+    # at this step length would add a fifth to the step time.
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step(False)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps
+    # kernel durations for the roofline: the same K steps again, with an event
+    # pair around every launch on the stream it is launched on
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
 
     qp_ms = [a.elapsed_time(b) for a, b in events["qp"][:used["qp"]]]
     at_ms = [a.elapsed_time(b) for a, b in events["attn"][:used["attn"]]]

@@ -123,6 +123,27 @@ __device__ inline int local_block(const Bounds &B, int r) {
     return lb;
 }
 
+// Blocks of a thread's QP_ITEMS consecutive rows r0 .. r0 + QP_ITEMS - 1:
+// the block of r0 and a mask with bit k set where row r0 + k starts a block
+// (block starts are distinct, so the block of row r0 + k is lb0 plus the set
+// bits 1 .. k). Rows past the unit's end stay in its last block.
+struct RowBlocks {
+    int lb0;
+    uint32_t starts;
+};
+
+__device__ inline RowBlocks row_blocks(const Bounds &B, int r0) {
+    RowBlocks R;
+    R.lb0 = local_block(B, r0);
+    R.starts = 0;
+#pragma unroll
+    for (int j = 0; j < QP_MAX_PACK - 1; ++j) {
+        const int d = B.b[j] - r0;
+        if (d > 0 && d < QP_ITEMS) R.starts |= 1u << d;
+    }
+    return R;
+}
+
 // Work-group barrier that orders LDS only. __syncthreads() also waits for
 // every outstanding global load (vmcnt), which would drain the next unit's
 // prefetch at each barrier; no wave here reads global memory another wave of
@@ -201,20 +222,18 @@ __device__ inline void unit_absmax(const QuantPackArgs &a, const Unit &U, const 
         flush_max(sh_max, 0, L, m);
         return;
     }
-    int cur = 0;
+    // rows past n repeat row n-1, which lies in the last block
+    const RowBlocks R = row_blocks(B, L.rr * QP_ITEMS);
+    int cur = R.lb0;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
-        const int r = L.rr * QP_ITEMS + k;
-        if (r < U.n) {
-            const int lb = local_block(B, r);          // non-decreasing in k
-            if (lb != cur) {
-                flush_max(sh_max, cur, L, m);
+        if (k > 0 && ((R.starts >> k) & 1u)) {
+            flush_max(sh_max, cur, L, m);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) m[j] = u16x2{0, 0};
-                cur = lb;
-            }
-            absmax_item(m, v[k]);
+            for (int j = 0; j < 4; ++j) m[j] = u16x2{0, 0};
+            ++cur;
         }
+        absmax_item(m, v[k]);
     }
     flush_max(sh_max, cur, L, m);
 }
@@ -275,11 +294,22 @@ __device__ inline void item_codes(const QuantPackArgs &a, const Unit &U, const B
 }
 
 // Words of unit U formed in registers, written to LDS as sh_w[plane * wp + row].
-template <int BITS, bool SIMPLE>
+// MODE: QM_SIMPLE one block, scales in s8/y8, every scale allows the
+// division-free quotient; QM_PACK several blocks, every scale of the unit
+// allows it (scales reloaded where a thread's rows enter the next block);
+// QM_GENERIC anything else (per-row block lookup and per-channel choice).
+enum { QM_SIMPLE = 0, QM_PACK = 1, QM_GENERIC = 2 };
+
+template <int BITS, int MODE>
 __device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 (&v)[QP_ITEMS],
                                    const Lane &L, int slot, const float *sh_s, const float *sh_y,
                                    float (&s8)[8], float (&y8)[8], int cur, bool fast, uint32_t *sh_w, int wp) {
-    constexpr uint32_t MASK = (1u << BITS) - 1u;
+    RowBlocks R = {0, 0u};
+    if constexpr (MODE == QM_PACK) {
+        R = row_blocks(B, L.rr * QP_ITEMS);
+        cur = R.lb0;
+        if (L.active) load_sy(sh_s, sh_y, cur, L, s8, y8);
+    }
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
         const int r = L.rr * QP_ITEMS + k;
@@ -287,35 +317,47 @@ __device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const 
         uint32_t f[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) f[j] = 0;
-        if (SIMPLE) {
+        if constexpr (MODE == QM_SIMPLE) {
             // rows past n repeat row n-1; their fields are discarded below
             item_codes<true>(a, U, B, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, fast, f);
+        } else if constexpr (MODE == QM_PACK) {
+            if (k > 0 && ((R.starts >> k) & 1u)) {
+                ++cur;
+                if (L.active) load_sy(sh_s, sh_y, cur, L, s8, y8);
+            }
+            codes8<true>(v[k], s8, y8, f);
         } else if (live) {
             item_codes<false>(a, U, B, v[k], L, r, slot, sh_s, sh_y, s8, y8, cur, fast, f);
         }
+        // Fields enter a word from the top: alignbit(f, w, BITS) = (w >> BITS) |
+        // (f << (32 - BITS)) keeps exactly the low BITS bits of f, so after the
+        // last field, field j sits at bit BITS * j plus whatever room is left
+        // below (32 - BITS * fields); one instruction per field.
         if constexpr (BITS == 4) {
             uint32_t w = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) w |= (f[j] & MASK) << (4 * j);
+            for (int j = 0; j < 8; ++j) w = __builtin_amdgcn_alignbit(f[j], w, 4);
             if (live) sh_w[L.chunk * wp + r] = w;
         } else if constexpr (BITS == 7 || BITS == 8) {
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                w0 |= (f[j] & MASK) << (BITS * j);
-                w1 |= (f[4 + j] & MASK) << (BITS * j);
+                w0 = __builtin_amdgcn_alignbit(f[j], w0, BITS);
+                w1 = __builtin_amdgcn_alignbit(f[4 + j], w1, BITS);
             }
+            if constexpr (BITS == 7) { w0 >>= 4; w1 >>= 4; }     // 28 bits used
             if (live) {
                 sh_w[(2 * L.chunk) * wp + r] = w0;
                 sh_w[(2 * L.chunk + 1) * wp + r] = w1;
             }
         } else if constexpr (BITS == 2) {
-            uint32_t half = 0;
+            uint32_t half = 0;      // this lane's 16 bits in the upper half
 #pragma unroll
-            for (int j = 0; j < 8; ++j) half |= (f[j] & MASK) << (2 * j);
+            for (int j = 0; j < 8; ++j) half = __builtin_amdgcn_alignbit(f[j], half, 2);
             // chunk ^ 1 of the same row: lane tid ^ 1 (rows hold an even number of lanes)
             const uint32_t other = (uint32_t)__shfl_xor((int)half, 1);
-            if (live && (L.chunk & 1) == 0) sh_w[(L.chunk >> 1) * wp + r] = half | (other << 16);
+            // low half from this lane's upper half, high half from the partner's
+            if (live && (L.chunk & 1) == 0) sh_w[(L.chunk >> 1) * wp + r] = (half >> 16) | (other & 0xFFFF0000u);
         }
     }
 }
@@ -340,13 +382,44 @@ __device__ inline void stage_codes(const QuantPackArgs &a, const Unit &U, const 
     }
 }
 
+// Store the staged words sh_w[plane * wp + row] of unit U, consecutive lanes
+// on consecutive tokens of a plane. When a plane's rows fit the work-group a
+// thread keeps one row and steps over planes, with several LDS reads in
+// flight before their stores.
+__device__ inline void store_words(const QuantPackArgs &a, const Unit &U, const uint32_t *sh_w, int wp, int tshift) {
+    const int tid = threadIdx.x;
+    const int span = 1 << tshift;
+    if (span <= QP_THREADS) {
+        const int r = tid & (span - 1);
+        if (r >= U.n) return;
+        const int P = QP_THREADS >> tshift;
+        int w = tid >> tshift;
+        const uint32_t *src = sh_w + w * wp + r;
+        uint32_t *dst = word_at(a, U, w, r);
+        const int sstep = P * wp;
+        const int64_t gstep = (int64_t)P * a.L_cap;
+#pragma unroll 4
+        for (; w < a.W; w += P) {
+            *dst = *src;
+            src += sstep;
+            dst += gstep;
+        }
+    } else {
+        for (int i = tid; i < a.W * span; i += QP_THREADS) {
+            const int w = i >> tshift, r = i & (span - 1);
+            if (r < U.n) *word_at(a, U, w, r) = sh_w[w * wp + r];
+        }
+    }
+}
+
 // Quantize and store unit U (rows in v) with the scales of LDS slot `slot`
-// (packs: slot = local block). Ends with a barrier, after which LDS may be
-// rewritten.
+// (packs: slot = local block). pack_fast: every scale of the unit is known to
+// allow the division-free quotient. Ends with a barrier, after which LDS may
+// be rewritten.
 template <int BITS>
 __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 (&v)[QP_ITEMS],
                                      const Lane &L, int slot, const float *sh_s, const float *sh_y,
-                                     uint8_t *sh_codes) {
+                                     uint8_t *sh_codes, bool pack_fast = false) {
     constexpr int CPW = 32 / BITS;
     const int tid = threadIdx.x;
     const int D = a.D;
@@ -371,14 +444,12 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
         // x rows 8 apart) then write distinct banks.
         uint32_t *sh_w = reinterpret_cast<uint32_t *>(sh_codes);
         const int wp = a.chunk_rows + 1;
-        if (simple) stage_words<BITS, true>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
-        else stage_words<BITS, false>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
+        if (simple) stage_words<BITS, QM_SIMPLE>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
+        else if (U.nb > 1 && pack_fast) stage_words<BITS, QM_PACK>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
+        else stage_words<BITS, QM_GENERIC>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
         lds_barrier();
         wait_loads();
-        for (int i = tid; i < a.W * span; i += QP_THREADS) {
-            const int w = i >> tshift, r = i & (span - 1);
-            if (r < U.n) *word_at(a, U, w, r) = sh_w[w * wp + r];
-        }
+        store_words(a, U, sh_w, wp, tshift);
         lds_barrier();
         return;
     }
@@ -496,12 +567,15 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
     for (int i = tid; i < QP_MAX_PACK * D; i += QP_THREADS) sh_max[i] = 0;
 
     if constexpr (!SPLIT) {
+        // set when a scale of the current unit needs IEEE division
+        __shared__ uint32_t sh_slow;
         lds_barrier();
         for (int64_t u = blockIdx.x; u < a.n_units; u += step) {
             const Unit U = unit_of(a, L.tb, u);
             uint4 X[QP_ITEMS];
             load_unit(a, U, X, L);
             const Bounds B = bounds_of(L.tb, U);
+            if (tid == 0) sh_slow = 0;
             unit_absmax(a, U, B, X, L, sh_max);
             lds_barrier();
             // scales of the unit's blocks, (block, channel) pairs over all threads
@@ -510,10 +584,12 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
                 const float m = u2f(sh_max[i]);
                 sh_max[i] = 0;
                 const int lb = i / D, c = i - lb * D;
-                scl[i] = put_scale<BITS>(sh_s, sh_y, lb, D, c, m);
+                const float sc = put_scale<BITS>(sh_s, sh_y, lb, D, c, m);
+                scl[i] = sc;
+                if (!fast_scale_ok(sc)) sh_slow = 1;
             }
             lds_barrier();
-            quantize_unit<BITS>(a, U, B, X, L, 0, sh_s, sh_y, sh_codes);
+            quantize_unit<BITS>(a, U, B, X, L, 0, sh_s, sh_y, sh_codes, sh_slow == 0);
         }
         return;
     }
