@@ -405,21 +405,31 @@ __device__ inline void store_words(const QuantPackArgs &a, const Unit &U, const 
             dst += gstep;
         }
     } else {
-        for (int i = tid; i < a.W * span; i += QP_THREADS) {
-            const int w = i >> tshift, r = i & (span - 1);
-            if (r < U.n) *word_at(a, U, w, r) = sh_w[w * wp + r];
+        // more rows than threads: rows tid, tid + QP_THREADS, ... of every plane
+        for (int r = tid; r < U.n; r += QP_THREADS) {
+            const uint32_t *src = sh_w + r;
+            uint32_t *dst = word_at(a, U, 0, r);
+#pragma unroll 4
+            for (int w = 0; w < a.W; ++w) {
+                *dst = *src;
+                src += wp;
+                dst += a.L_cap;
+            }
         }
     }
 }
 
 // Quantize and store unit U (rows in v) with the scales of LDS slot `slot`
 // (packs: slot = local block). pack_fast: every scale of the unit is known to
-// allow the division-free quotient. Ends with a barrier, after which LDS may
-// be rewritten.
-template <int BITS>
+// allow the division-free quotient. WHOLE (the whole-block kernel): no load
+// is in flight, so the stores need not wait for any (otherwise they wait for
+// the prefetch first, and the next unit then waits for no store). Ends with a
+// barrier, after which LDS may be rewritten.
+template <int BITS, bool WHOLE = false>
 __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 (&v)[QP_ITEMS],
                                      const Lane &L, int slot, const float *sh_s, const float *sh_y,
                                      uint8_t *sh_codes, bool pack_fast = false) {
+    constexpr bool drain = !WHOLE;
     constexpr int CPW = 32 / BITS;
     const int tid = threadIdx.x;
     const int D = a.D;
@@ -448,7 +458,7 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
         else if (U.nb > 1 && pack_fast) stage_words<BITS, QM_PACK>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
         else stage_words<BITS, QM_GENERIC>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
         lds_barrier();
-        wait_loads();
+        if (drain) wait_loads();
         store_words(a, U, sh_w, wp, tshift);
         lds_barrier();
         return;
@@ -459,7 +469,7 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
     if (simple) stage_codes<BITS, true>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_codes, pitch);
     else stage_codes<BITS, false>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_codes, pitch);
     lds_barrier();
-    wait_loads();
+    if (drain) wait_loads();
     for (int i = tid; i < a.W * span; i += QP_THREADS) {
         const int w = i >> tshift, r = i & (span - 1);
         if (r >= U.n) continue;
@@ -589,7 +599,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
                 if (!fast_scale_ok(sc)) sh_slow = 1;
             }
             lds_barrier();
-            quantize_unit<BITS>(a, U, B, X, L, 0, sh_s, sh_y, sh_codes, sh_slow == 0);
+            quantize_unit<BITS, true>(a, U, B, X, L, 0, sh_s, sh_y, sh_codes, sh_slow == 0);
         }
         return;
     }
