@@ -28,7 +28,10 @@ Readings where the pages are silent (each listed in the design notes):
     fp32 [B, H, G_cap, D];
   * dequantized value bf16_rne(fp32(q) * s);
   * attention over the whole window [0, L_kv) without a mask, logits scaled by
-    the fp32 softmax scale (default fp32(1/sqrt(D))), computed here in fp64.
+    the fp32 softmax scale (default fp32(1/sqrt(D))), computed here in fp64;
+  * grouping variants (Table 5, Table 1): the "channel axis" is the hidden
+    width H * D, so groupings without it share a scale across heads; scales
+    are stored compactly, one fp32 per group.
 
 Array conventions: activations are float32 arrays holding bf16 values, in the
 BLHc layout [B, L, H, D] (the README's qkv_format "BLHc"). Words are uint32.
@@ -324,3 +327,94 @@ def fake_quant(x, offsets, bits, per_channel=True) -> np.ndarray:
         q = np.clip(np.rint(r), -qm, qm).astype(np.float32)
         out[:, off[g]:off[g + 1]] = bf16_round_f32((q * s).astype(np.float32))
     return out
+
+
+# --------------------------------------------------------------------------
+# Grouping variants of project page Table 5 (and Table 1): where one scale is
+# shared. The "channel axis" is the whole hidden width H * D: a grouping
+# without it shares a scale across heads as well as head channels. This is the
+# reading that reproduces every VAR-d30 KV-cache size of Table 5 from its
+# scale count (10.44 / 9.45 / 9.34 / 10.51 / 9.38 GB).
+# --------------------------------------------------------------------------
+
+GROUPINGS = ("channel_block", "channel", "block", "token_head", "token", "tensor")
+
+
+def grouping_scale_shape(mode, B, L, H, D, G):
+    """Compact scale layout of each grouping (one fp32 per group):
+    channel_block [B, H, G, D] (VAR-Q, Table 5 "VAR-Q (full)"), channel [B, H, D]
+    ("without block axis"), block [B, G] ("without channel axis"), token_head
+    [B, H, L] ("per-token & per-head"), token [B, L] ("per-token"), tensor [1]
+    (Table 1 "per-tensor")."""
+    return {"channel_block": (B, H, G, D), "channel": (B, H, D), "block": (B, G),
+            "token_head": (B, H, L), "token": (B, L), "tensor": (1,)}[mode]
+
+
+def grouping_ids(mode, B, L, H, D, offsets) -> np.ndarray:
+    """Flat index into the compact scale layout of every element of x [B, L, H, D];
+    int64 [B, L, H, D]."""
+    off = _check_offsets(offsets, L)
+    G = len(off) - 1
+    g_of_t = np.zeros(L, dtype=np.int64)
+    for g in range(G):
+        g_of_t[off[g]:off[g + 1]] = g
+    b = np.arange(B, dtype=np.int64)[:, None, None, None]
+    t = np.arange(L, dtype=np.int64)[None, :, None, None]
+    h = np.arange(H, dtype=np.int64)[None, None, :, None]
+    c = np.arange(D, dtype=np.int64)[None, None, None, :]
+    g = g_of_t[None, :, None, None]
+    ids = {"channel_block": ((b * H + h) * G + g) * D + c,
+           "channel": (b * H + h) * D + c,
+           "block": b * G + g + 0 * (h + c),
+           "token_head": (b * H + h) * L + t + 0 * c,
+           "token": b * L + t + 0 * (h + c),
+           "tensor": 0 * (b + t + h + c)}[mode]
+    return np.broadcast_to(ids, (B, L, H, D)).astype(np.int64)
+
+
+def grouped_scales(x, mode, offsets, bits) -> np.ndarray:
+    """s = fp32(absmax / qmax) per group of `mode`; float32 of grouping_scale_shape."""
+    x = np.asarray(x, dtype=np.float32)
+    B, L, H, D = x.shape
+    G = len(_check_offsets(offsets, L)) - 1
+    shape = grouping_scale_shape(mode, B, L, H, D, G)
+    a = np.zeros(int(np.prod(shape)), dtype=np.float32)
+    np.maximum.at(a, grouping_ids(mode, B, L, H, D, offsets).ravel(), np.abs(x).ravel())
+    return (a / np.float32(qmax(bits))).astype(np.float32).reshape(shape)
+
+
+def grouped_codes(x, mode, offsets, scales, bits) -> np.ndarray:
+    """Codes q = clip(rint(fp32(x / s)), -qmax, qmax) with each element's group
+    scale (q = 0 where s = 0); int32 [B, H, L, D]."""
+    x = np.asarray(x, dtype=np.float32)
+    B, L, H, D = x.shape
+    s = np.asarray(scales, dtype=np.float32).ravel()[grouping_ids(mode, B, L, H, D, offsets)]
+    safe = np.where(s == 0, np.float32(1), s)
+    r = np.where(s == 0, np.float32(0), np.divide(x, safe, dtype=np.float32))
+    qm = qmax(bits)
+    return np.clip(np.rint(r), -qm, qm).astype(np.int32).transpose(0, 2, 1, 3)
+
+
+def grouped_quantize_pack(x, mode, offsets, bits):
+    """Quantize+pack with the scales of grouping `mode`: (words uint32 [B, H, W, L],
+    scales float32 of grouping_scale_shape). The words are laid out exactly like
+    the channel x block cache; only where a scale is shared differs."""
+    s = grouped_scales(x, mode, offsets, bits)
+    return pack_codes(grouped_codes(x, mode, offsets, s, bits), bits), s
+
+
+def grouped_dequantize(words, scales, mode, offsets, head_dim, bits) -> np.ndarray:
+    """bf16_rne(fp32(q) * s) with each element's group scale; float32 [B, L, H, D]."""
+    q = unpack_words(words, head_dim, bits).transpose(0, 2, 1, 3)     # [B, L, H, D]
+    B, L, H, D = q.shape
+    s = np.asarray(scales, dtype=np.float32).ravel()[grouping_ids(mode, B, L, H, D, offsets)]
+    return bf16_round_f32((q.astype(np.float32) * s).astype(np.float32))
+
+
+def grouped_kv_gib(mode, seqs, L, C, D, G, bits, layers) -> float:
+    """KV-cache size in GiB of `layers` K and V caches of `seqs` sequences of L
+    tokens and C = H * D hidden channels: b-bit codes without padding plus one
+    4-byte scale per group (project page, Table 5 "KV (GB)" columns)."""
+    H = C // D
+    n_scales = int(np.prod(grouping_scale_shape(mode, seqs, L, H, D, G)))
+    return 2 * layers * (seqs * L * C * bits / 8 + 4 * n_scales) / 2 ** 30

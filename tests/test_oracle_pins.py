@@ -404,3 +404,125 @@ def test_reduction_rejects_alternative_layouts():
     assert abs(var_batch_shared - 72.06) > 1.0
     sf_int6_pad_free = 100.0 * (1.0 - (32.0 / 5) / 16.0 - 4.0 * 21 / (2.0 * 32760))
     assert abs(sf_int6_pad_free - 59.25) > 0.5
+
+
+# ---------------------------------------------------------------- grouping variants (Table 5 / Table 1)
+
+def _golden_grouping():
+    import json
+    import os
+    return json.load(open(os.path.join(os.path.dirname(__file__), "golden", "grouping_kv_table5.json")))
+
+
+def test_grouping_kv_sizes_match_table5():
+    """Project page Table 5, KV (GB): the scale count of each grouping, with
+    unpadded 4-bit codes, reproduces the printed cache sizes."""
+    gold = _golden_grouping()
+    for row in gold["rows"]:
+        if not row["pinned"]:
+            continue
+        geo = gold[row["model"]]
+        gib = O.grouped_kv_gib(row["mode"], geo["seqs"], geo["L"], geo["C"], geo["D"], geo["G"],
+                               geo["bits"], geo["layers"])
+        assert round(gib, 2) == row["gb"], (row, gib)
+
+
+def test_grouping_kv_alternative_readings_fail():
+    """The other plausible reading of 'without channel axis' (one scale per
+    (batch, head, block)) misses Table 5's VAR value, so the pin above decides it."""
+    gold = _golden_grouping()
+    geo = gold["var"]
+    H = geo["C"] // geo["D"]
+    per_head_block = 2 * geo["layers"] * (geo["seqs"] * geo["L"] * geo["C"] * 4 / 8
+                                          + 4 * geo["seqs"] * H * geo["G"]) / 2 ** 30
+    assert round(per_head_block, 2) != 9.34
+
+
+def _brute_grouped(x, mode, offsets, bits):
+    """Element loops with explicit group keys (no index arithmetic shared with the oracle)."""
+    B, L, H, D = x.shape
+    def key(b, t, h, c):
+        g = max(i for i in range(len(offsets) - 1) if offsets[i] <= t)
+        return {"channel_block": (b, h, g, c), "channel": (b, h, c), "block": (b, g),
+                "token_head": (b, h, t), "token": (b, t), "tensor": ()}[mode]
+    amax = {}
+    for b in range(B):
+        for t in range(L):
+            for h in range(H):
+                for c in range(D):
+                    k = key(b, t, h, c)
+                    amax[k] = max(amax.get(k, 0.0), abs(float(x[b, t, h, c])))
+    qm = O.qmax(bits)
+    scale = {k: np.float32(np.float32(a) / np.float32(qm)) for k, a in amax.items()}
+    codes = np.zeros((B, H, L, D), dtype=np.int64)
+    for b in range(B):
+        for t in range(L):
+            for h in range(H):
+                for c in range(D):
+                    s = scale[key(b, t, h, c)]
+                    codes[b, h, t, c] = 0 if s == 0 else int(np.rint(np.float32(np.float32(x[b, t, h, c]) / s)))
+    return scale, codes, key
+
+
+def test_grouped_oracle_matches_brute_force():
+    rng = np.random.RandomState(3)
+    B, L, H, D = 2, 9, 3, 12
+    offsets = [0, 1, 4, 9]
+    x = O.bf16_round_f32(rng.randn(B, L, H, D).astype(np.float32) * 3)
+    x[1, 4:9, 2, :] = 0                                     # an all-zero group in several modes
+    for bits in (3, 4, 8):
+        for mode in O.GROUPINGS:
+            words, s = O.grouped_quantize_pack(x, mode, offsets, bits)
+            scale, codes, key = _brute_grouped(x, mode, offsets, bits)
+            ids = O.grouping_ids(mode, B, L, H, D, offsets)
+            flat = s.ravel()
+            for b in range(B):
+                for t in range(L):
+                    for h in range(H):
+                        for c in range(D):
+                            assert flat[ids[b, t, h, c]] == scale[key(b, t, h, c)]
+            assert np.array_equal(O.unpack_words(words, D, bits), codes), (mode, bits)
+            assert s.size == len(scale), (mode, s.size, len(scale))
+
+
+def test_grouped_reduces_to_channel_block_and_each_other():
+    rng = np.random.RandomState(4)
+    B, L, H, D = 2, 11, 3, 16
+    offsets = [0, 2, 6, 11]
+    x = O.bf16_round_f32(rng.randn(B, L, H, D).astype(np.float32))
+    # channel x block is the plain quantize+pack operator
+    w0, s0 = O.quantize_pack(x, offsets, 4)
+    w1, s1 = O.grouped_quantize_pack(x, "channel_block", offsets, 4)
+    assert np.array_equal(w0, w1) and np.array_equal(s0, s1)
+    # without block axis is channel x block over one block [0, L)
+    w0, s0 = O.quantize_pack(x, [0, L], 4)
+    w1, s1 = O.grouped_quantize_pack(x, "channel", offsets, 4)
+    assert np.array_equal(w0, w1) and np.array_equal(s0[:, :, 0, :], s1)
+    # one head: per-token equals per-token & per-head; one block: per-block equals per-tensor when B = 1
+    xh = x[:, :, :1]
+    assert np.array_equal(O.grouped_quantize_pack(xh, "token", offsets, 4)[0],
+                          O.grouped_quantize_pack(xh, "token_head", offsets, 4)[0])
+    x1 = x[:1]
+    assert np.array_equal(O.grouped_quantize_pack(x1, "block", [0, L], 4)[0],
+                          O.grouped_quantize_pack(x1, "tensor", offsets, 4)[0])
+    # dequantize inverts the scale layout: channel x block through grouped_dequantize
+    w, s = O.grouped_quantize_pack(x, "channel_block", offsets, 4)
+    assert np.array_equal(O.grouped_dequantize(w, s, "channel_block", offsets, D, 4).transpose(0, 2, 1, 3),
+                          O.unpack_dequant(w, s, offsets, D, 4))
+
+
+def test_table1_ordering_through_grouped_modes():
+    """Project page Table 1 on the next-scale outlier generator, with the
+    grouping maps of Table 5: per-tensor > per-block > per-channel > channel x
+    block in relative Frobenius error, for K and for V."""
+    from synth import WORKLOADS, workload_inputs
+    wl = WORKLOADS["tiny"]
+    k, v, _ = workload_inputs(wl, seed=0)
+    for t in (k, v):
+        x = t.float().numpy()
+        errs = []
+        for mode in ("tensor", "block", "channel", "channel_block"):
+            w, s = O.grouped_quantize_pack(x, mode, list(wl.offsets), 4)
+            xq = O.grouped_dequantize(w, s, mode, list(wl.offsets), x.shape[3], 4)
+            errs.append(np.linalg.norm(xq - x) / np.linalg.norm(x))
+        assert errs[0] > errs[1] > errs[2] > errs[3], errs
