@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run 5 plain device-to-device copies of BYTES bytes (counter calibration)")
+    p.add_argument("--grouping-report", action="store_true",
+                   help="only time quantize+pack of K under every scale grouping (one JSON line)")
     return p.parse_args()
 
 
@@ -204,6 +206,62 @@ def unfused_compare(varq, torch, wl, bits, launches, off, q, pk, sk, pv, sv, arg
             "fused_speedup": round(ms / fused_ms, 3) if fused_ms else None}
 
 
+# ---------------------------------------------------------------- grouping report
+
+def grouping_report(varq, torch, wl, bits, k, args):
+    """quantize+pack of the workload's K under each scale grouping of the
+    project page's Table 5 / Table 1, event-timed per launch. Algorithmic bytes
+    count one read of K plus the words and scales written (the groupings other
+    than channel x block and channel read K twice)."""
+    B, L, H, D = k.shape
+    G = len(wl.offsets) - 1
+    W = varq.words_per_row(D, bits)
+    packed = torch.zeros(B, H, W, varq.round_capacity(L), dtype=torch.int32, device=k.device)
+    modes = {}
+    for mode in varq.GROUPINGS:
+        scales = torch.zeros(varq.grouped_scale_shape(mode, B, L, H, D, G), dtype=torch.float32, device=k.device)
+        fn = lambda: varq.quantize_pack_grouped(k, list(wl.offsets), bits, mode, packed, scales)
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        nbytes = B * L * H * D * 2 + B * H * W * L * 4 + scales.numel() * 4
+        modes[mode] = {"avg_ms": round(ms, 5), "alg_bytes": nbytes, "scales": scales.numel(),
+                       "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    maps = {}
+    if wl.kind == "next_frame":
+        # channel x block with other boundary maps: the 4680-token chunk
+        # (compression ratio 3) and 1560-token frames shifted by half a frame
+        scales = torch.zeros(B, H, L // 780 + 2, D, dtype=torch.float32, device=k.device)
+        for tag, off in (("frames_1560", varq.frame_group_offsets(L, 1560)),
+                         ("chunk_4680", varq.frame_group_offsets(L, 4680)),
+                         ("frames_1560_misaligned", varq.frame_group_offsets(L, 1560, phase=780))):
+            fn = lambda: varq.quantize_pack(k, off, bits, packed, scales)
+            for _ in range(max(1, args.warmup)):
+                fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+            nbytes = qp_bytes(B, L, H, D, len(off) - 1, bits)
+            maps[tag] = {"blocks": len(off) - 1, "avg_ms": round(ms, 5), "alg_bytes": nbytes,
+                         "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    print(json.dumps({"grouping_report": {"workload": wl.name, "bits": bits, "tensor": "K",
+                                          "shape": [B, L, H, D], "blocks": G, "steps": args.steps,
+                                          "modes": modes, "boundary_maps": maps}}))
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -227,6 +285,10 @@ def main():
     wl = WORKLOADS[args.workload]
     bits = args.bits or wl.bits[0]
     dev = torch.device("cuda:0")
+    if args.grouping_report:
+        k, _, _ = workload_inputs(wl, seed=0, device=dev, with_v=False)
+        grouping_report(varq, torch, wl, bits, k, args)
+        return
     k, v, q = workload_inputs(wl, seed=0, device=dev)
     off = list(wl.offsets)
     B, H, D, L, G = wl.B, wl.H, wl.D, wl.L, wl.G

@@ -113,6 +113,61 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
                        void *stream);
 
 /*
+ * Scale groupings (project page, grouping ablation Table 5 and error table
+ * Table 1). The "channel axis" is the hidden width H * D: a grouping without
+ * it shares one scale across heads and head channels. Compact fp32 scale
+ * layouts, one value per group:
+ *   VARQ_GROUP_CHANNEL_BLOCK  [B, H, G, D]  the method (varq_quantize_pack)
+ *   VARQ_GROUP_CHANNEL        [B, H, D]     "without block axis" (one block [0, L))
+ *   VARQ_GROUP_BLOCK          [B, G]        "without channel axis"
+ *   VARQ_GROUP_TOKEN_HEAD     [B, H, L]     "per-token & per-head"
+ *   VARQ_GROUP_TOKEN          [B, L]        "per-token"
+ *   VARQ_GROUP_TENSOR         [1]           "per-tensor" (Table 1)
+ */
+enum {
+    VARQ_GROUP_CHANNEL_BLOCK = 0,
+    VARQ_GROUP_CHANNEL = 1,
+    VARQ_GROUP_BLOCK = 2,
+    VARQ_GROUP_TOKEN_HEAD = 3,
+    VARQ_GROUP_TOKEN = 4,
+    VARQ_GROUP_TENSOR = 5
+};
+
+/* Number of scales of grouping `mode` for x [B, L, H, D] with G blocks
+ * (the product of the layout above); -1 for an unknown mode or a negative size. */
+int64_t varq_grouped_scale_count(int mode, int B, int64_t L, int H, int D, int G);
+
+/*
+ * quantize+pack with the scales of grouping `mode` (project page Table 5):
+ * for every group, a = max |x| over its elements and s = fp32(a/qmax); codes,
+ * packing and word layout are exactly those of varq_quantize_pack. Quantizes
+ * one whole sequence window [0, L) (no append offsets).
+ *
+ *  x            bf16 [B, L, H, D] at element strides (sx_b, sx_l, sx_h), channel
+ *               stride 1. Pointer 16-byte aligned; strides multiples of 8.
+ *  group_offsets host int32[G+1] block boundaries (used by CHANNEL_BLOCK and
+ *               BLOCK; the other groupings still require a valid table).
+ *  packed       int32 [B, H, W, L_cap], rows [0, L) written. 16-byte aligned;
+ *               L_cap % 8 == 0, L <= L_cap.
+ *  scales       fp32, n_scales >= varq_grouped_scale_count(...) entries; the first
+ *               count are written (compact layout above). 4-byte aligned. For
+ *               BLOCK, TOKEN_HEAD, TOKEN and TENSOR the buffer first holds the
+ *               groups' maxima while the call runs (stream-ordered).
+ *  D            head_dim: a multiple of 8, 8 <= D <= 256.
+ * CHANNEL_BLOCK and CHANNEL run varq_quantize_pack (its scratch rules apply);
+ * the other groupings run three passes over x and allocate nothing.
+ * Errors: VARQ_EBITS, VARQ_EINVAL (unknown mode, bad sizes or table),
+ * VARQ_EALIGN, VARQ_ECAPACITY (L > L_cap or n_scales too small),
+ * VARQ_EUNSUPPORTED (B*L*H*W or the scale count beyond 2^31 - 1), VARQ_ELAUNCH.
+ * Deterministic.
+ */
+int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
+                               int B, int H, int D, int64_t L,
+                               int mode, const int32_t *group_offsets, int G, int bits,
+                               int32_t *packed, int64_t L_cap,
+                               float *scales, int64_t n_scales, void *stream);
+
+/*
  * Packed-KV attention (project page "Next-block prediction": a block attends to
  * the cache of all earlier blocks and itself; README: packed-KV load, unpack and
  * dequant fused into attention). For every (b, h) and query row i:

@@ -8,13 +8,18 @@ plain bf16 attention over dense K/V for the unfused comparison. The module
 
 from . import varq  # noqa: F401
 from .varq import (  # noqa: F401
+    GROUPINGS,
     VarqError,
     alloc_cache,
     bf16_attention,
     cache_bytes,
     codes_per_word,
+    frame_group_offsets,
+    grouped_scale_count,
+    grouped_scale_shape,
     packed_attention,
     quantize_pack,
+    quantize_pack_grouped,
     unpack_dequant,
     words_per_row,
 )

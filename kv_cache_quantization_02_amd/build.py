@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvarq.so")
 SELFTEST_LIB = os.path.join(HERE, "libvarq_selftest.so")
 
-LIB_SOURCES = ["varq_api.cpp", "quant_pack.hip", "unpack_dequant.hip", "packed_attention.hip"]
+LIB_SOURCES = ["varq_api.cpp", "quant_pack.hip", "quant_group.hip", "unpack_dequant.hip", "packed_attention.hip"]
 SELFTEST_SOURCES = ["quant_math_selftest.cpp"]
 
 HIP_FLAGS = [

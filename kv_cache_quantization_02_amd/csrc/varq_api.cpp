@@ -23,6 +23,7 @@ int quant_pack_max_pack();
 hipError_t launch_unpack_dequant(const UnpackArgs &a, int bits, hipStream_t st);
 hipError_t launch_packed_attention(const AttnArgs &a, int D, int bits, hipStream_t st);
 hipError_t launch_dense_attention(const AttnArgs &a, int D, hipStream_t st);
+hipError_t launch_quant_group(const GroupArgs &a, int mode, int bits, int64_t n_scales, hipStream_t st);
 int attention_q_tile();
 }  // namespace varq
 
@@ -264,6 +265,70 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
     }
     return launch_status(varq::launch_quant_pack(a, bits, grid, split, static_cast<hipStream_t>(stream)),
                          "quantize_pack");
+}
+
+int64_t varq_grouped_scale_count(int mode, int B, int64_t L, int H, int D, int G) {
+    if (B < 0 || L < 0 || H < 0 || D < 0 || G < 0) return -1;
+    switch (mode) {
+        case VARQ_GROUP_CHANNEL_BLOCK: return (int64_t)B * H * G * D;
+        case VARQ_GROUP_CHANNEL: return (int64_t)B * H * D;
+        case VARQ_GROUP_BLOCK: return (int64_t)B * G;
+        case VARQ_GROUP_TOKEN_HEAD: return (int64_t)B * H * L;
+        case VARQ_GROUP_TOKEN: return (int64_t)B * L;
+        case VARQ_GROUP_TENSOR: return 1;
+        default: return -1;
+    }
+}
+
+int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
+                               int B, int H, int D, int64_t L,
+                               int mode, const int32_t *group_offsets, int G, int bits,
+                               int32_t *packed, int64_t L_cap,
+                               float *scales, int64_t n_scales, void *stream) {
+    if (int r = check_bits(bits)) return r;
+    if (mode < VARQ_GROUP_CHANNEL_BLOCK || mode > VARQ_GROUP_TENSOR)
+        return fail(VARQ_EINVAL, "quantize_pack_grouped: unknown grouping %d", mode);
+    if (B < 1 || H < 1 || L < 1)
+        return fail(VARQ_EINVAL, "quantize_pack_grouped: B=%d H=%d L=%lld must be >= 1", B, H, (long long)L);
+    if (D < 8 || D > 256 || D % 8 != 0)
+        return fail(VARQ_EINVAL, "quantize_pack_grouped: head_dim %d must be a multiple of 8 in 8..256", D);
+    if (int r = check_offsets(group_offsets, G, L, "quantize_pack_grouped")) return r;
+    const int64_t count = varq_grouped_scale_count(mode, B, L, H, D, G);
+    if (n_scales < count)
+        return fail(VARQ_ECAPACITY, "quantize_pack_grouped: n_scales=%lld < %lld scales of grouping %d",
+                    (long long)n_scales, (long long)count, mode);
+    if (mode == VARQ_GROUP_CHANNEL_BLOCK)
+        return varq_quantize_pack(x, sx_b, sx_l, sx_h, B, H, D, L, group_offsets, G, bits, packed, L_cap, 0,
+                                  scales, G, 0, stream);
+    if (mode == VARQ_GROUP_CHANNEL) {
+        const int32_t whole[2] = {0, (int32_t)L};
+        return varq_quantize_pack(x, sx_b, sx_l, sx_h, B, H, D, L, whole, 1, bits, packed, L_cap, 0,
+                                  scales, 1, 0, stream);
+    }
+    if (!x || !packed || !scales) return fail(VARQ_EINVAL, "quantize_pack_grouped: NULL tensor pointer");
+    if (!aligned(x, 16) || sx_b % 8 || sx_l % 8 || sx_h % 8)
+        return fail(VARQ_EALIGN, "quantize_pack_grouped: x must be 16-byte aligned with strides that are multiples of 8");
+    if (!aligned(packed, 16) || L_cap % 8)
+        return fail(VARQ_EALIGN, "quantize_pack_grouped: packed must be 16-byte aligned and L_cap a multiple of 8");
+    if (!aligned(scales, 4)) return fail(VARQ_EALIGN, "quantize_pack_grouped: scales must be 4-byte aligned");
+    if (L > L_cap)
+        return fail(VARQ_ECAPACITY, "quantize_pack_grouped: L=%lld exceeds L_cap=%lld", (long long)L, (long long)L_cap);
+    const int W = words_per_row(D, bits);
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    if ((int64_t)B * L * H * W > lim || (int64_t)B * L * H * (D / 8) > lim || count > lim)
+        return fail(VARQ_EUNSUPPORTED, "quantize_pack_grouped: B*L*H*W or the scale count exceeds 2^31 - 1");
+
+    varq::GroupArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = static_cast<const uint16_t *>(x);
+    a.sx_b = sx_b; a.sx_l = sx_l; a.sx_h = sx_h;
+    a.packed = reinterpret_cast<uint32_t *>(packed);
+    a.absmax = reinterpret_cast<uint32_t *>(scales);
+    a.L_cap = L_cap;
+    a.B = B; a.L = (int)L; a.H = H; a.D = D; a.W = W; a.G = G;
+    for (int g = 0; g <= G; ++g) a.off[g] = group_offsets[g];
+    return launch_status(varq::launch_quant_group(a, mode, bits, count, static_cast<hipStream_t>(stream)),
+                         "quantize_pack_grouped");
 }
 
 int varq_unpack_dequant(const int32_t *packed, const float *scales,

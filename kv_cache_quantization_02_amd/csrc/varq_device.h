@@ -47,6 +47,16 @@ struct UnpackArgs {
     int32_t off[VARQ_MAX_GROUPS_DEV + 1];
 };
 
+struct GroupArgs {
+    const uint16_t *x;          // bf16 [B, L, H, D] at (sx_b, sx_l, sx_h)
+    int64_t sx_b, sx_l, sx_h;
+    uint32_t *packed;           // [B, H, W, L_cap]
+    uint32_t *absmax;           // the scale buffer: group maxima (fp32 bits), then scales
+    int64_t L_cap;
+    int B, L, H, D, W, G;
+    int32_t off[VARQ_MAX_GROUPS_DEV + 1];
+};
+
 struct AttnArgs {
     const uint16_t *q;          // bf16 [B, Lq, H, D]
     int64_t sq_b, sq_l, sq_h;

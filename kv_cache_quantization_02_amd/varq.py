@@ -45,6 +45,9 @@ _SIGNATURES = {
                                    _vp, _vp]),
     "varq_bf16_attention": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _vp, _vp, _i64, _i64,
                                    _f32, _vp, _i64, _i64, _i64, _vp]),
+    "varq_grouped_scale_count": (_i64, [_i32, _i32, _i64, _i32, _i32, _i32]),
+    "varq_quantize_pack_grouped": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i32, _i32p, _i32,
+                                          _i32, _vp, _i64, _vp, _i64, _vp]),
     "varq_last_error": (ctypes.c_char_p, []),
     "varq_version": (ctypes.c_char_p, []),
 }
@@ -150,6 +153,52 @@ def quantize_pack(x, group_offsets, bits, packed, scales, tok_start=0, group_sta
         x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, H, D, L, off, G, bits,
         packed.data_ptr(), packed.shape[3], tok_start, scales.data_ptr(), scales.shape[2],
         group_start, _stream(stream, x.device)))
+    return packed, scales
+
+
+def frame_group_offsets(L, group_tokens, phase=0):
+    """Block boundaries for a next-frame cache of L tokens in groups of
+    `group_tokens` (project page: 1560-token frame groups; a compression ratio
+    of 3 makes the whole 4680-token chunk one group). phase > 0 shifts every
+    interior boundary by `phase` tokens (Table 6's misaligned placement uses
+    half a group), which leaves a shorter group at each end."""
+    L, g, phase = int(L), int(group_tokens), int(phase)
+    if L < 1 or g < 1 or not 0 <= phase < g:
+        raise ValueError("need L >= 1, group_tokens >= 1 and 0 <= phase < group_tokens")
+    inner = list(range(phase if phase else g, L, g))
+    return [0] + [b for b in inner if 0 < b < L] + [L]
+
+
+# Scale groupings of the project page's Table 5 / Table 1 (include/varq.h VARQ_GROUP_*)
+GROUPINGS = {"channel_block": 0, "channel": 1, "block": 2, "token_head": 3, "token": 4, "tensor": 5}
+
+
+def grouped_scale_shape(mode, B, L, H, D, G):
+    """Compact scale layout of a grouping (one fp32 per group)."""
+    return {"channel_block": (B, H, G, D), "channel": (B, H, D), "block": (B, G),
+            "token_head": (B, H, L), "token": (B, L), "tensor": (1,)}[mode]
+
+
+def grouped_scale_count(mode, B, L, H, D, G):
+    return lib().varq_grouped_scale_count(GROUPINGS[mode], B, L, H, D, G)
+
+
+def quantize_pack_grouped(x, group_offsets, bits, mode, packed, scales, stream=None):
+    """x bf16 [B, L, H, D] -> rows [0, L) of `packed` [B, H, W, L_cap] and the
+    compact scales of grouping `mode` (a contiguous fp32 tensor of at least
+    grouped_scale_count(...) elements)."""
+    _need(x, torch.bfloat16, "x")
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float32, "scales")
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("x must be [B, L, H, D] with channel stride 1")
+    if not packed.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("packed and scales must be contiguous")
+    B, L, H, D = x.shape
+    off, G = _offsets(group_offsets)
+    _check(lib().varq_quantize_pack_grouped(
+        x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, H, D, L, GROUPINGS[mode], off, G, bits,
+        packed.data_ptr(), packed.shape[3], scales.data_ptr(), scales.numel(), _stream(stream, x.device)))
     return packed, scales
 
 

@@ -182,3 +182,57 @@ def test_kernel_code_arithmetic_exhaustive(selftest, bits):
 def test_kernel_dequant_arithmetic(selftest, bits):
     # scales across the whole exponent range, subnormals included
     assert selftest.varq_selftest_dequant(bits, 0x0001, 0x7F00) == 0
+
+
+def _qpg(V, **kw):
+    a = dict(x=0x10000, sx_b=680 * 16 * 64, sx_l=16 * 64, sx_h=64, B=1, H=16, D=64, L=680,
+             mode=3, off=[0, 1, 5, 680], bits=4, packed=0x20000, L_cap=680, scales=0x30000,
+             n_scales=16 * 680)
+    a.update(kw)
+    off = (ctypes.c_int32 * len(a["off"]))(*a["off"])
+    return V.lib().varq_quantize_pack_grouped(a["x"], a["sx_b"], a["sx_l"], a["sx_h"], a["B"], a["H"], a["D"],
+                                              a["L"], a["mode"], off, len(a["off"]) - 1, a["bits"], a["packed"],
+                                              a["L_cap"], a["scales"], a["n_scales"], None)
+
+
+def test_grouped_scale_count_matches_oracle(V):
+    import numpy as np
+    for mode, code in V.GROUPINGS.items():
+        for (B, L, H, D, G) in ((1, 680, 16, 64, 10), (3, 37, 5, 40, 4)):
+            assert V.grouped_scale_count(mode, B, L, H, D, G) == \
+                int(np.prod(O.grouping_scale_shape(mode, B, L, H, D, G)))
+            assert V.grouped_scale_shape(mode, B, L, H, D, G) == O.grouping_scale_shape(mode, B, L, H, D, G)
+    assert V.lib().varq_grouped_scale_count(7, 1, 1, 1, 8, 1) == -1
+
+
+def test_quantize_pack_grouped_validation(V):
+    assert _qpg(V, bits=9) == -2
+    assert _qpg(V, mode=6) == -1 and _qpg(V, mode=-1) == -1    # unknown grouping
+    assert _qpg(V, off=[0, 5, 600]) == -1                      # offsets must end at L
+    assert _qpg(V, D=60) == -1
+    assert _qpg(V, n_scales=16 * 680 - 1) == -4                # per-token & per-head needs B*H*L
+    assert _qpg(V, mode=5, n_scales=0) == -4                   # per-tensor needs one
+    assert _qpg(V, x=0x10008) == -3 and _qpg(V, sx_l=16 * 64 + 4) == -3
+    assert _qpg(V, packed=0x20004) == -3 and _qpg(V, L_cap=684) == -3
+    assert _qpg(V, scales=0x30002) == -3
+    assert _qpg(V, L_cap=672) == -4                            # rows beyond the cache
+    assert _qpg(V, x=0) == -1
+    # the channel groupings go through quantize_pack's own checks
+    assert _qpg(V, mode=0, n_scales=16 * 3 * 64, L_cap=672) == -4
+    assert _qpg(V, mode=1, n_scales=16 * 64, packed=0x20004) == -3
+    assert _qpg(V, mode=4, n_scales=10) == -4 and "n_scales" in V.last_error()
+
+
+def test_frame_group_offsets(V):
+    """Next-frame group maps: 1560-token frames, the 4680-token chunk, and the
+    half-frame shift of the misaligned placement (same sizes inside, a half
+    group at each end)."""
+    assert V.frame_group_offsets(4680, 1560) == [0, 1560, 3120, 4680]
+    assert V.frame_group_offsets(4680, 4680) == [0, 4680]
+    assert V.frame_group_offsets(4680, 1560, phase=780) == [0, 780, 2340, 3900, 4680]
+    assert V.frame_group_offsets(100, 30) == [0, 30, 60, 90, 100]
+    off = V.frame_group_offsets(32760, 1560, phase=780)
+    sizes = [b - a for a, b in zip(off, off[1:])]
+    assert sizes[0] == sizes[-1] == 780 and set(sizes[1:-1]) == {1560}
+    with pytest.raises(ValueError):
+        V.frame_group_offsets(100, 30, phase=30)

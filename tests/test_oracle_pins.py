@@ -526,3 +526,32 @@ def test_table1_ordering_through_grouped_modes():
             xq = O.grouped_dequantize(w, s, mode, list(wl.offsets), x.shape[3], 4)
             errs.append(np.linalg.norm(xq - x) / np.linalg.norm(x))
         assert errs[0] > errs[1] > errs[2] > errs[3], errs
+
+
+def test_grouping_error_report_is_the_oracles():
+    """tests/golden/grouping_errors.json comes from grouping_error_report.py
+    (oracle only): the small workload's rows recompute exactly, and every
+    stored workload keeps project page Table 1's K and V ordering per-tensor >
+    per-block > per-channel > channel x block."""
+    import importlib.util
+    import json
+    import os
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    spec = importlib.util.spec_from_file_location("grouping_error_report", os.path.join(here, "grouping_error_report.py"))
+    rep = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(rep)
+    stored = json.load(open(os.path.join(here, "grouping_errors.json")))
+    fresh = rep.report("tiny")
+    for mode, e in stored["workloads"]["tiny"]["errors"].items():
+        for col in ("k", "v", "attention", "output"):
+            assert abs(e[col] - fresh["errors"][mode][col]) <= 1e-12 * max(1.0, abs(e[col])), (mode, col)
+    for name, w in stored["workloads"].items():
+        e = w["errors"]
+        for col in ("k", "v"):
+            vals = [e[m][col] for m in ("tensor", "block", "channel", "channel_block")]
+            assert vals[0] > vals[1] > vals[2] > vals[3], (name, col, vals)
+    # Table 6 direction: frame-aligned groups beat the same groups shifted by half
+    # a frame, and 1560-token frames beat the 4680-token chunk
+    b = stored["boundaries"]["maps"]
+    for col in ("k", "v", "output"):
+        assert b["frames_1560"][col] < b["frames_1560_misaligned"][col] < b["chunk_4680"][col], col
