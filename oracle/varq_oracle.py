@@ -31,7 +31,11 @@ Readings where the pages are silent (each listed in the design notes):
     the fp32 softmax scale (default fp32(1/sqrt(D))), computed here in fp64;
   * grouping variants (Table 5, Table 1): the "channel axis" is the hidden
     width H * D, so groupings without it share a scale across heads; scales
-    are stored compactly, one fp32 per group.
+    are stored compactly, one fp32 per group;
+  * pre-RoPE quantization (Appendix F, Table 7): K is quantized before the
+    rotation; the dequantized bf16 K is rotated pairwise, (2i, 2i+1), by
+    per-token cos/sin tables in fp32 (each product and the sum rounded) and
+    rounded to bf16 again; the query arrives already rotated.
 
 Array conventions: activations are float32 arrays holding bf16 values, in the
 BLHc layout [B, L, H, D] (the README's qkv_format "BLHc"). Words are uint32.
@@ -418,3 +422,48 @@ def grouped_kv_gib(mode, seqs, L, C, D, G, bits, layers) -> float:
     H = C // D
     n_scales = int(np.prod(grouping_scale_shape(mode, seqs, L, H, D, G)))
     return 2 * layers * (seqs * L * C * bits / 8 + 4 * n_scales) / 2 ** 30
+
+
+# --------------------------------------------------------------------------
+# Pre-RoPE quantization (project page, Appendix F / Table 7 and Insight 03,
+# Eq. 3): K is quantized before the rotary embedding, and the rotation is
+# applied to the dequantized K just before attention. RoPE rotates every
+# channel pair (2i, 2i+1) by an angle that depends on the token's position;
+# the schedule is given as per-token tables cos[t, i], sin[t, i].
+# --------------------------------------------------------------------------
+
+def rope_tables(positions, head_dim, base=10000.0):
+    """The standard one-axis schedule: angle(t, i) = positions[t] * base^(-2i/D),
+    cos and sin computed in fp64 and rounded to fp32; float32 [L, D/2] each."""
+    pos = np.asarray(positions, dtype=np.float64)[:, None]
+    inv = base ** (-2.0 * np.arange(head_dim // 2, dtype=np.float64) / head_dim)
+    ang = pos * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def apply_rope(x, cos, sin) -> np.ndarray:
+    """Rotate the pairs (2i, 2i+1) of x [..., L, D] (bf16 values) by the table
+    angles of each token: a' = a*c - b*s, b' = a*s + b*c, each product and the
+    sum rounded to fp32, then the result rounded to bf16. float32 [..., L, D]."""
+    x = np.asarray(x, dtype=np.float32)
+    c = np.asarray(cos, dtype=np.float32)
+    s = np.asarray(sin, dtype=np.float32)
+    a, b = x[..., 0::2], x[..., 1::2]
+    a2 = (a * c).astype(np.float32) - (b * s).astype(np.float32)
+    b2 = (a * s).astype(np.float32) + (b * c).astype(np.float32)
+    out = np.empty_like(x)
+    out[..., 0::2] = bf16_round_f32(a2.astype(np.float32))
+    out[..., 1::2] = bf16_round_f32(b2.astype(np.float32))
+    return out
+
+
+def packed_attention_rope(q, words_k, scales_k, words_v, scales_v, offsets, bits, cos, sin,
+                          softmax_scale=None, bh=None):
+    """Attention over a cache whose K was quantized before RoPE: K^ is
+    dequantized, rotated by the tables (apply_rope) and only then used; q is
+    the already rotated query. Returns what attention_fp64 returns."""
+    B, Lq, H, D = np.asarray(q).shape
+    khat = apply_rope(unpack_dequant(words_k, scales_k, offsets, D, bits), cos, sin)
+    vhat = unpack_dequant(words_v, scales_v, offsets, D, bits)
+    sig = default_softmax_scale(D) if softmax_scale is None else np.float32(softmax_scale)
+    return attention_fp64(q, khat, vhat, sig, bh)

@@ -555,3 +555,78 @@ def test_grouping_error_report_is_the_oracles():
     b = stored["boundaries"]["maps"]
     for col in ("k", "v", "output"):
         assert b["frames_1560"][col] < b["frames_1560_misaligned"][col] < b["chunk_4680"][col], col
+
+
+# ---------------------------------------------------------------- pre-RoPE quantization (Table 7, Eq. 3)
+
+def test_apply_rope_special_angles_are_exact():
+    """Zero angle is the identity; a quarter turn maps (a, b) to (-b, a); a half
+    turn negates both channels (project page Insight 03: RoPE rotates pairs)."""
+    rng = np.random.RandomState(5)
+    x = O.bf16_round_f32(rng.randn(3, 7, 16).astype(np.float32))
+    L, P = 7, 8
+    one, zero = np.ones((L, P), np.float32), np.zeros((L, P), np.float32)
+    assert np.array_equal(O.apply_rope(x, one, zero), x)
+    r = O.apply_rope(x, zero, one)
+    assert np.array_equal(r[..., 0::2], -x[..., 1::2]) and np.array_equal(r[..., 1::2], x[..., 0::2])
+    h = O.apply_rope(x, -one, zero)
+    assert np.array_equal(h, -x)
+
+
+def test_apply_rope_preserves_pair_norm_and_composes():
+    """Eq. 3 / Appendix C: a rotation keeps each pair's l2 norm; rotating by
+    angles u then w equals rotating by u + w (both within bf16 rounding)."""
+    rng = np.random.RandomState(6)
+    x = O.bf16_round_f32(rng.randn(4, 9, 32).astype(np.float32) * 3)
+    cu, su = O.rope_tables(np.arange(9) * 3 + 1, 32)
+    cw, sw = O.rope_tables(np.arange(9) * 5 + 2, 32)
+    cuw, suw = O.rope_tables(np.arange(9) * 8 + 3, 32)
+    r1 = O.apply_rope(x, cu, su)
+    n0 = np.hypot(x[..., 0::2], x[..., 1::2])
+    n1 = np.hypot(r1[..., 0::2], r1[..., 1::2])
+    assert np.allclose(n1, n0, rtol=2 ** -7, atol=1e-6)
+    r2 = O.apply_rope(r1, cw, sw)
+    r12 = O.apply_rope(x, cuw, suw)
+    assert np.allclose(r2, r12, rtol=2 ** -6, atol=2 ** -6 * np.abs(x).max())
+
+
+def test_rope_scores_depend_only_on_position_differences():
+    """The textbook property of rotary embeddings: with Q and K rotated by the
+    same one-axis schedule, shifting every position by a constant leaves the
+    logits unchanged (here up to the bf16 rounding of the rotated vectors)."""
+    rng = np.random.RandomState(7)
+    D, L = 64, 24
+    q = O.bf16_round_f32(rng.randn(L, D).astype(np.float32))
+    k = O.bf16_round_f32(rng.randn(L, D).astype(np.float32))
+    pos = np.arange(L)
+    s0 = O.apply_rope(q, *O.rope_tables(pos, D)).astype(np.float64) @ O.apply_rope(k, *O.rope_tables(pos, D)).T
+    s1 = O.apply_rope(q, *O.rope_tables(pos + 37, D)).astype(np.float64) @ O.apply_rope(k, *O.rope_tables(pos + 37, D)).T
+    assert np.abs(s0 - s1).max() <= 0.05 * np.abs(s0).max()
+    # and the logit of one query/key pair equals the rotation of q by the position difference
+    qd = O.apply_rope(q[None, 5], *O.rope_tables([5 - 11], D))[0].astype(np.float64)
+    assert abs(qd @ k[11] - s0[5, 11]) <= 0.05 * np.abs(s0).max()
+
+
+def test_pre_rope_attention_reduces_to_post_rope_for_identity_tables():
+    """With cos = 1, sin = 0 pre-RoPE attention is the plain packed attention."""
+    from synth import WORKLOADS, workload_inputs
+    wl = WORKLOADS["tiny"]
+    k, v, q = workload_inputs(wl, seed=0)
+    k, v, q = k.float().numpy(), v.float().numpy(), q.float().numpy()
+    off = list(wl.offsets)
+    wk, sk = O.quantize_pack(k, off, 4)
+    wv, sv = O.quantize_pack(v, off, 4)
+    L, D = k.shape[1], k.shape[3]
+    one, zero = np.ones((L, D // 2), np.float32), np.zeros((L, D // 2), np.float32)
+    a = O.packed_attention_rope(q, wk, sk, wv, sv, off, 4, one, zero, bh=[(0, 3)])
+    b = O.packed_attention(q, wk, sk, wv, sv, off, 4, bh=[(0, 3)])
+    assert np.array_equal(a[0], b[0])
+
+
+def test_rope_tables_against_closed_form_angles():
+    """Position 0 has angle 0 in every pair; pair 0 turns by exactly one radian
+    per position; the last pair's frequency is base^(-(D-2)/D)."""
+    c, s = O.rope_tables(np.arange(5), 8, base=10000.0)
+    assert np.array_equal(c[0], np.ones(4, np.float32)) and np.array_equal(s[0], np.zeros(4, np.float32))
+    assert np.allclose(c[:, 0], np.cos(np.arange(5)), atol=1e-7) and np.allclose(s[:, 0], np.sin(np.arange(5)), atol=1e-7)
+    assert abs(np.arctan2(s[1, 3], c[1, 3]) - 10000.0 ** (-6 / 8)) < 1e-7
