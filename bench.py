@@ -50,6 +50,9 @@ def parse():
                    help="only run 5 plain device-to-device copies of BYTES bytes (counter calibration)")
     p.add_argument("--grouping-report", action="store_true",
                    help="only time quantize+pack of K under every scale grouping (one JSON line)")
+    p.add_argument("--pre-rope-report", action="store_true",
+                   help="only time the last attention call with K quantized before RoPE against the "
+                        "plain (post-RoPE) kernel (one JSON line)")
     return p.parse_args()
 
 
@@ -262,6 +265,64 @@ def grouping_report(varq, torch, wl, bits, k, args):
                                           "modes": modes, "boundary_maps": maps}}))
 
 
+# ---------------------------------------------------------------- pre-RoPE report
+
+def pre_rope_report(varq, torch, wl, bits, args):
+    """The workload's last attention call three ways, event-timed per call: the
+    plain packed attention (post-RoPE cache, the method's default), the same
+    call on a cache quantized before RoPE with the rotation applied to every
+    dequantized K tile (project page Appendix F / Table 7), and the unfused
+    pre-RoPE path (unpack_dequant_rope + unpack_dequant + bf16_attention)."""
+    from synth import gen_next_scale_kv, gen_pre_rope_frame_k, gen_queries, rope_frame_tables
+    dev = torch.device("cuda:0")
+    off = list(wl.offsets)
+    if wl.kind == "next_frame":
+        k, cos, sin = gen_pre_rope_frame_k(wl.B, wl.H, wl.D, off, 0, 1, dev)
+    else:
+        k = gen_next_scale_kv(wl.B, wl.H, wl.D, off, wl.n_out_k, 0, 1, dev, shared_across_batch=True)
+        cos, sin = rope_frame_tables(wl.L, wl.D, dev)
+    v = gen_next_scale_kv(wl.B, wl.H, wl.D, off, wl.n_out_v, 0, 2, dev, shared_across_batch=False)
+    q0, ql, L_kv = wl.calls[-1]
+    q = gen_queries(wl.B, ql, wl.H, wl.D, 0, 3, dev)
+    B, H, D = wl.B, wl.H, wl.D
+    pk, sk = varq.alloc_cache(B, H, D, wl.L, len(off) - 1, bits, device=dev)
+    pv, sv = varq.alloc_cache(B, H, D, wl.L, len(off) - 1, bits, device=dev)
+    varq.quantize_pack(k, off, bits, pk, sk)
+    varq.quantize_pack(v, off, bits, pv, sv)
+    del k, v
+    goff = off[:off.index(L_kv) + 1]
+    out = torch.empty_like(q)
+    kd = torch.empty(B, H, L_kv, D, dtype=torch.bfloat16, device=dev)
+    vd = torch.empty_like(kd)
+
+    def timeit(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+
+    def unfused():
+        varq.unpack_dequant_rope(pk, sk, goff, bits, cos, sin, out=kd)
+        varq.unpack_dequant(pv, sv, goff, bits, out=vd)
+        varq.bf16_attention(q, kd, vd, out=out)
+
+    t_post = timeit(lambda: varq.packed_attention(q, pk, sk, pv, sv, goff, bits, out=out))
+    t_pre = timeit(lambda: varq.packed_attention_rope(q, pk, sk, pv, sv, goff, bits, cos, sin, out=out))
+    t_unf = timeit(unfused)
+    flops = attn_flops(B, H, D, ql, L_kv)
+    rows = {name: {"avg_ms": round(t, 5), "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 2)}
+            for name, t in (("post_rope_fused", t_post), ("pre_rope_fused", t_pre), ("pre_rope_unfused", t_unf))}
+    print(json.dumps({"pre_rope_report": {"workload": wl.name, "bits": bits, "call": [q0, ql, L_kv],
+                                          "steps": args.steps, "calls": rows,
+                                          "rotation_overhead": round(t_pre / t_post - 1.0, 4)}}))
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -285,6 +346,9 @@ def main():
     wl = WORKLOADS[args.workload]
     bits = args.bits or wl.bits[0]
     dev = torch.device("cuda:0")
+    if args.pre_rope_report:
+        pre_rope_report(varq, torch, wl, bits, args)
+        return
     if args.grouping_report:
         k, _, _ = workload_inputs(wl, seed=0, device=dev, with_v=False)
         grouping_report(varq, torch, wl, bits, k, args)

@@ -113,6 +113,40 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
                        void *stream);
 
 /*
+ * Pre-RoPE quantization (project page Appendix F / Table 7; Insight 03, Eq. 3):
+ * the cache holds K quantized BEFORE the rotary embedding, and the rotation is
+ * applied to the dequantized K. The schedule is a pair of fp32 tables
+ * rope_cos, rope_sin [L, D/2] (row t = cache token t, column i = channel pair
+ * (2i, 2i+1)), device pointers, 4-byte aligned, at least L (unpack) or L_kv
+ * (attention) rows. For every pair of the dequantized bf16 values (a, b):
+ *   a' = bf16_rne(fp32(fp32(a*c) - fp32(b*s))),  b' = bf16_rne(fp32(fp32(a*s) + fp32(b*c))).
+ *
+ * varq_unpack_dequant_rope: varq_unpack_dequant followed by that rotation
+ * (the unfused pre-RoPE path; bit-exact). Same arguments and errors as
+ * varq_unpack_dequant, plus VARQ_EINVAL for a NULL table and VARQ_EALIGN.
+ *
+ * varq_packed_attention_rope: varq_packed_attention with every dequantized K
+ * tile rotated before the scores; q must already be rotated (it is not
+ * cached). Same arguments, errors and tolerance as varq_packed_attention,
+ * plus VARQ_EINVAL for a NULL table and VARQ_EALIGN.
+ */
+int varq_unpack_dequant_rope(const int32_t *packed, const float *scales,
+                             int B, int H, int D, int64_t L_cap, int64_t G_cap, int64_t L,
+                             const int32_t *group_offsets, int G, int bits,
+                             const float *rope_cos, const float *rope_sin,
+                             void *out, void *stream);
+
+int varq_packed_attention_rope(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
+                               int B, int H, int D, int64_t Lq,
+                               const int32_t *packed_k, const float *scales_k,
+                               const int32_t *packed_v, const float *scales_v,
+                               int64_t L_cap, int64_t G_cap, int64_t L_kv,
+                               const int32_t *group_offsets, int G, int bits,
+                               float softmax_scale,
+                               void *out, int64_t so_b, int64_t so_l, int64_t so_h,
+                               const float *rope_cos, const float *rope_sin, void *stream);
+
+/*
  * Scale groupings (project page, grouping ablation Table 5 and error table
  * Table 1). The "channel axis" is the hidden width H * D: a grouping without
  * it shares one scale across heads and head channels. Compact fp32 scale

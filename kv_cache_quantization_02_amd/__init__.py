@@ -18,8 +18,10 @@ from .varq import (  # noqa: F401
     grouped_scale_count,
     grouped_scale_shape,
     packed_attention,
+    packed_attention_rope,
     quantize_pack,
     quantize_pack_grouped,
     unpack_dequant,
+    unpack_dequant_rope,
     words_per_row,
 )

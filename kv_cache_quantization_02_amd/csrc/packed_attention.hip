@@ -96,7 +96,11 @@ __device__ inline int v_pos(int tok) {
 // SL: the (batch, head)'s K and V scales (at most AT_SL_MAXG blocks) are
 // copied to LDS once, and dequantization reads them there; otherwise each
 // tile's scales are prefetched from memory with its words.
-template <int BITS, int D, int QB, int NW, bool SL>
+// ROPE (pre-RoPE quantization, project page Appendix F / Table 7): K was
+// quantized before the rotary embedding; every dequantized K tile is rotated
+// in LDS, pair (2i, 2i+1) of token t by cos/sin[t, i] (fp32, each product and
+// the sum rounded, then bf16), before the scores use it.
+template <int BITS, int D, int QB, int NW, bool SL, bool ROPE = false>
 __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a) {
     using T = AttnTile<BITS, D, QB, NW>;
     constexpr bool DENSE = T::DENSE;
@@ -491,9 +495,29 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         }
     };
 
+    // pre-RoPE: rotate the K pairs of the tile in LDS buffer `buf` (tokens past
+    // L_kv take the last row's angles; the scores mask them)
+    auto rope_tile = [&](int buf, int n0) {
+        uint16_t *K = Ks + buf * KBUF;
+        constexpr int HALF = D / 2, PAIRS = AT_NT * HALF;
+#pragma unroll
+        for (int p0 = 0; p0 < PAIRS; p0 += THREADS) {
+            const int p = p0 + tid;
+            const int tok = p / HALF, i = p - tok * HALF;
+            const int64_t trow = (int64_t)min(n0 + tok, L_kv - 1) * HALF + i;
+            const float c = a.rcos[trow], s = a.rsin[trow];
+            uint32_t *kp = reinterpret_cast<uint32_t *>(K + tok * KP + 2 * i);
+            const uint32_t v = *kp;
+            const float x0 = bf16lo(v), x1 = bf16hi(v);
+            const float c0 = x0 * c, c1 = x1 * s, c2 = x0 * s, c3 = x1 * c;
+            *kp = pack_bf16x2(c0 - c1, c2 + c3);
+        }
+    };
+
     // ---------------- pipeline: LDS-only barrier (global prefetches stay in
     // flight); tile jt + 2 is prefetched while tile jt is computed and tile
-    // jt + 1 dequantized into the other LDS buffer.
+    // jt + 1 dequantized into the other LDS buffer. With ROPE, a tile is
+    // rotated in place (one more barrier) before its compute.
     auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
     int jt = 0;
     prefetch(P0, 0);
@@ -503,12 +527,20 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     for (; jt + 1 < nt; ++jt) {
         const int cur = jt & 1;
         const int n0 = jt * AT_NT;
+        if constexpr (ROPE) {
+            rope_tile(cur, n0);
+            lds_barrier();
+        }
         // with EARLY_S the next tile's dequantization follows this tile's
         // compute and overlaps its last matrix ops; otherwise it goes first
         if constexpr (EARLY_S) compute(cur, n0, false);
         dequant(cur ^ 1, P0, n0 + AT_NT);
         if (jt + 2 < nt) prefetch(P0, n0 + 2 * AT_NT);
         if constexpr (!EARLY_S) compute(cur, n0, false);
+        lds_barrier();
+    }
+    if constexpr (ROPE) {
+        rope_tile(jt & 1, jt * AT_NT);
         lds_barrier();
     }
     compute(jt & 1, jt * AT_NT, true);
@@ -549,6 +581,11 @@ template <int BITS, int D>
 static hipError_t launch_at(const AttnArgs &a, hipStream_t st) {
     const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H;
     const int64_t grid = (n_blocks + 7) / 8 * 8;
+    if (a.rcos) {
+        hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW, false, true>), dim3((unsigned)grid),
+                           dim3(64 * AT_CFG_NW), 0, st, a);
+        return hipGetLastError();
+    }
     // head_dim 64 keeps up to AT_SL_MAXG blocks' scales in LDS (LDS still
     // fits two work-groups per CU); otherwise scales stream with the words
     if (D == 64 && a.G <= AT_SL_MAXG)

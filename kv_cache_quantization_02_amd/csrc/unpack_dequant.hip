@@ -6,14 +6,16 @@
 //
 // One thread writes one 16-byte chunk (8 channels) of one output row, so the
 // stores of a wave are contiguous; the 1-3 words a chunk needs are read from
-// their planes.
+// their planes. ROPE (pre-RoPE quantization, project page Appendix F): the
+// chunk's four channel pairs (2i, 2i+1) are then rotated by cos/sin[t, i]
+// (fp32, each product and the sum rounded) and rounded to bf16 again.
 #include "varq_device.h"
 
 namespace varq {
 
 constexpr int UD_THREADS = 256;
 
-template <int BITS>
+template <int BITS, bool ROPE>
 __global__ __launch_bounds__(UD_THREADS) void unpack_dequant_kernel(const UnpackArgs a) {
     constexpr int CPW = 32 / BITS;
     constexpr uint32_t MASK = (1u << BITS) - 1u;
@@ -54,6 +56,14 @@ __global__ __launch_bounds__(UD_THREADS) void unpack_dequant_kernel(const Unpack
             (void)MASK;
             bits2[e] = dequant_bits(q, srow[c]);
         }
+        if constexpr (ROPE) {
+            const int64_t trow = t * (a.D >> 1) + 4 * j + (k >> 1);
+            const float c = a.rcos[trow], s = a.rsin[trow];
+            const float x0 = u2f(bits2[0] << 16), x1 = u2f(bits2[1] << 16);
+            const float c0 = x0 * c, c1 = x1 * s, c2 = x0 * s, c3 = x1 * c;
+            bits2[0] = bf16_bits_rne(c0 - c1);
+            bits2[1] = bf16_bits_rne(c2 + c3);
+        }
         outw[k >> 1] = bits2[0] | (bits2[1] << 16);
     }
     uint4 *dst = reinterpret_cast<uint4 *>(a.out + rowid * a.D + 8 * j);
@@ -64,7 +74,10 @@ template <int BITS>
 static hipError_t launch_ud(const UnpackArgs &a, hipStream_t st) {
     const int64_t total = (int64_t)a.B * a.H * a.L * (a.D >> 3);
     const int64_t grid = (total + UD_THREADS - 1) / UD_THREADS;
-    hipLaunchKernelGGL(unpack_dequant_kernel<BITS>, dim3((unsigned)grid), dim3(UD_THREADS), 0, st, a);
+    if (a.rcos)
+        hipLaunchKernelGGL((unpack_dequant_kernel<BITS, true>), dim3((unsigned)grid), dim3(UD_THREADS), 0, st, a);
+    else
+        hipLaunchKernelGGL((unpack_dequant_kernel<BITS, false>), dim3((unsigned)grid), dim3(UD_THREADS), 0, st, a);
     return hipGetLastError();
 }
 

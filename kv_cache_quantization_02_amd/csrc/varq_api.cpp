@@ -331,10 +331,12 @@ int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_
                          "quantize_pack_grouped");
 }
 
-int varq_unpack_dequant(const int32_t *packed, const float *scales,
+namespace {
+
+int unpack_dequant_impl(const int32_t *packed, const float *scales,
                         int B, int H, int D, int64_t L_cap, int64_t G_cap, int64_t L,
                         const int32_t *group_offsets, int G, int bits,
-                        void *out, void *stream) {
+                        const float *rcos, const float *rsin, void *out, void *stream) {
     if (int r = check_bits(bits)) return r;
     if (B < 1 || H < 1) return fail(VARQ_EINVAL, "unpack_dequant: B=%d H=%d must be >= 1", B, H);
     if (D < 8 || D > 256 || D % 8 != 0)
@@ -352,19 +354,46 @@ int varq_unpack_dequant(const int32_t *packed, const float *scales,
                     (long long)L, G, (long long)L_cap, (long long)G_cap);
     const int64_t items = (int64_t)B * H * L * (D / 8);
     if (items / 256 >= (1LL << 31)) return fail(VARQ_EINVAL, "unpack_dequant: tensor too large");
+    if (rcos && (!aligned(rcos, 4) || !aligned(rsin, 4)))
+        return fail(VARQ_EALIGN, "unpack_dequant_rope: rope tables must be 4-byte aligned");
 
     varq::UnpackArgs a;
     std::memset(&a, 0, sizeof(a));
     a.packed = reinterpret_cast<const uint32_t *>(packed);
     a.scales = scales;
     a.out = static_cast<uint16_t *>(out);
+    a.rcos = rcos; a.rsin = rsin;
     a.L_cap = L_cap; a.G_cap = G_cap; a.L = L;
     a.B = B; a.H = H; a.D = D; a.W = words_per_row(D, bits); a.G = G;
     for (int g = 0; g <= G; ++g) a.off[g] = group_offsets[g];
     return launch_status(varq::launch_unpack_dequant(a, bits, static_cast<hipStream_t>(stream)), "unpack_dequant");
 }
 
-int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
+}  // namespace
+
+int varq_unpack_dequant(const int32_t *packed, const float *scales,
+                        int B, int H, int D, int64_t L_cap, int64_t G_cap, int64_t L,
+                        const int32_t *group_offsets, int G, int bits,
+                        void *out, void *stream) {
+    return unpack_dequant_impl(packed, scales, B, H, D, L_cap, G_cap, L, group_offsets, G, bits, nullptr, nullptr,
+                               out, stream);
+}
+
+int varq_unpack_dequant_rope(const int32_t *packed, const float *scales,
+                             int B, int H, int D, int64_t L_cap, int64_t G_cap, int64_t L,
+                             const int32_t *group_offsets, int G, int bits,
+                             const float *rope_cos, const float *rope_sin,
+                             void *out, void *stream) {
+    if (!rope_cos || !rope_sin) return fail(VARQ_EINVAL, "unpack_dequant_rope: NULL rope table");
+    return unpack_dequant_impl(packed, scales, B, H, D, L_cap, G_cap, L, group_offsets, G, bits, rope_cos, rope_sin,
+                               out, stream);
+}
+
+namespace {
+
+// Packed attention; rcos/rsin non-null: K was quantized before RoPE and its
+// tiles are rotated after dequantization (tables [L_kv, D/2]).
+int packed_attention_impl(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
                           int B, int H, int D, int64_t Lq,
                           const int32_t *packed_k, const float *scales_k,
                           const int32_t *packed_v, const float *scales_v,
@@ -372,7 +401,7 @@ int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
                           const int32_t *group_offsets, int G, int bits,
                           float softmax_scale,
                           void *out, int64_t so_b, int64_t so_l, int64_t so_h,
-                          void *stream) {
+                          const float *rcos, const float *rsin, void *stream) {
     if (int r = check_bits(bits)) return r;
     if (B < 1 || H < 1) return fail(VARQ_EINVAL, "packed_attention: B=%d H=%d must be >= 1", B, H);
     if (D != 64 && D != 128)
@@ -396,6 +425,10 @@ int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
     if (L_kv > L_cap || G > G_cap)
         return fail(VARQ_ECAPACITY, "packed_attention: L_kv=%lld / G=%d exceed L_cap=%lld / G_cap=%lld",
                     (long long)L_kv, G, (long long)L_cap, (long long)G_cap);
+    if ((rcos == nullptr) != (rsin == nullptr))
+        return fail(VARQ_EINVAL, "packed_attention_rope: rope_cos and rope_sin must both be given");
+    if (rcos && (!aligned(rcos, 4) || !aligned(rsin, 4)))
+        return fail(VARQ_EALIGN, "packed_attention_rope: rope tables must be 4-byte aligned");
     const int qtile = varq::attention_q_tile();
     const int64_t n_qtiles = (Lq + qtile - 1) / qtile;
     if (n_qtiles * B * H >= (1LL << 31) - 8) return fail(VARQ_EINVAL, "packed_attention: grid too large");
@@ -413,9 +446,41 @@ int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
     a.B = B; a.H = H; a.W = words_per_row(D, bits); a.G = G;
     a.n_qtiles = (int)n_qtiles;
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    a.rcos = rcos; a.rsin = rsin;
     for (int g = 0; g <= G; ++g) a.off[g] = group_offsets[g];
     return launch_status(varq::launch_packed_attention(a, D, bits, static_cast<hipStream_t>(stream)),
                          "packed_attention");
+}
+
+}  // namespace
+
+int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
+                          int B, int H, int D, int64_t Lq,
+                          const int32_t *packed_k, const float *scales_k,
+                          const int32_t *packed_v, const float *scales_v,
+                          int64_t L_cap, int64_t G_cap, int64_t L_kv,
+                          const int32_t *group_offsets, int G, int bits,
+                          float softmax_scale,
+                          void *out, int64_t so_b, int64_t so_l, int64_t so_h,
+                          void *stream) {
+    return packed_attention_impl(q, sq_b, sq_l, sq_h, B, H, D, Lq, packed_k, scales_k, packed_v, scales_v,
+                                 L_cap, G_cap, L_kv, group_offsets, G, bits, softmax_scale, out, so_b, so_l, so_h,
+                                 nullptr, nullptr, stream);
+}
+
+int varq_packed_attention_rope(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
+                               int B, int H, int D, int64_t Lq,
+                               const int32_t *packed_k, const float *scales_k,
+                               const int32_t *packed_v, const float *scales_v,
+                               int64_t L_cap, int64_t G_cap, int64_t L_kv,
+                               const int32_t *group_offsets, int G, int bits,
+                               float softmax_scale,
+                               void *out, int64_t so_b, int64_t so_l, int64_t so_h,
+                               const float *rope_cos, const float *rope_sin, void *stream) {
+    if (!rope_cos || !rope_sin) return fail(VARQ_EINVAL, "packed_attention_rope: NULL rope table");
+    return packed_attention_impl(q, sq_b, sq_l, sq_h, B, H, D, Lq, packed_k, scales_k, packed_v, scales_v,
+                                 L_cap, G_cap, L_kv, group_offsets, G, bits, softmax_scale, out, so_b, so_l, so_h,
+                                 rope_cos, rope_sin, stream);
 }
 
 int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,

@@ -42,6 +42,7 @@ struct UnpackArgs {
     const uint32_t *packed;     // [B, H, W, L_cap]
     const float *scales;        // [B, H, G_cap, D]
     uint16_t *out;              // bf16 [B, H, L, D]
+    const float *rcos, *rsin;   // pre-RoPE: per-token rotation tables [L, D/2] (else null)
     int64_t L_cap, G_cap, L;
     int B, H, D, W, G;
     int32_t off[VARQ_MAX_GROUPS_DEV + 1];
@@ -63,6 +64,7 @@ struct AttnArgs {
     const uint32_t *pk, *pv;    // [B, H, W, L_cap]
     const float *sk, *sv;       // [B, H, G_cap, D]
     const uint16_t *kd, *vd;    // dense bf16 [B, H, L_cap, D] (unfused baseline; pk/pv unused)
+    const float *rcos, *rsin;   // pre-RoPE: per-token rotation tables [L_kv, D/2] (else null)
     uint16_t *out;              // bf16 [B, Lq, H, D]
     int64_t so_b, so_l, so_h;
     int64_t L_cap, G_cap, L_kv, Lq;

@@ -45,6 +45,11 @@ _SIGNATURES = {
                                    _vp, _vp]),
     "varq_bf16_attention": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _vp, _vp, _i64, _i64,
                                    _f32, _vp, _i64, _i64, _i64, _vp]),
+    "varq_unpack_dequant_rope": (_i32, [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32p, _i32, _i32,
+                                        _vp, _vp, _vp, _vp]),
+    "varq_packed_attention_rope": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64,
+                                          _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32p, _i32, _i32,
+                                          _f32, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "varq_grouped_scale_count": (_i64, [_i32, _i32, _i64, _i32, _i32, _i32]),
     "varq_quantize_pack_grouped": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i32, _i32p, _i32,
                                           _i32, _vp, _i64, _vp, _i64, _vp]),
@@ -234,6 +239,75 @@ def packed_attention(q, packed_k, scales_k, packed_v, scales_v, group_offsets, b
         packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
         packed_k.shape[3], scales_k.shape[2], L_kv, off, G, bits, softmax_scale,
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2), _stream(stream, q.device)))
+    return out
+
+
+def _rope_tables(rope_cos, rope_sin, rows, D):
+    for t, n in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        _need(t, torch.float32, n)
+        if not t.is_contiguous() or t.dim() != 2 or t.shape[1] != D // 2 or t.shape[0] < rows:
+            raise ValueError(f"{n} must be a contiguous fp32 [>= {rows}, {D // 2}] table")
+
+
+def packed_attention_rope(q, packed_k, scales_k, packed_v, scales_v, group_offsets, bits, rope_cos, rope_sin,
+                          softmax_scale=None, out=None, stream=None):
+    """packed_attention over a cache whose K was quantized before RoPE: each
+    dequantized K row t is rotated by rope_cos/rope_sin[t] (fp32 [>= L_kv, D/2])
+    before the scores; q is already rotated."""
+    _need(q, torch.bfloat16, "q")
+    for t, n in ((packed_k, "packed_k"), (packed_v, "packed_v")):
+        _need(t, torch.int32, n)
+    for t, n in ((scales_k, "scales_k"), (scales_v, "scales_v")):
+        _need(t, torch.float32, n)
+    if q.dim() != 4 or q.stride(3) != 1:
+        raise ValueError("q must be [B, Lq, H, D] with channel stride 1")
+    for t in (packed_k, packed_v, scales_k, scales_v):
+        if not t.is_contiguous():
+            raise ValueError("packed caches and scales must be contiguous")
+    if packed_k.shape != packed_v.shape or scales_k.shape != scales_v.shape:
+        raise ValueError("K and V caches must have the same geometry")
+    B, Lq, H, D = q.shape
+    L_kv = int(group_offsets[-1])
+    _rope_tables(rope_cos, rope_sin, L_kv, D)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    softmax_scale = float(np.float32(softmax_scale))
+    if out is None:
+        out = torch.empty(B, Lq, H, D, dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out")
+    if out.stride(3) != 1:
+        raise ValueError("out must have channel stride 1")
+    off, G = _offsets(group_offsets)
+    _check(lib().varq_packed_attention_rope(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), B, H, D, Lq,
+        packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
+        packed_k.shape[3], scales_k.shape[2], L_kv, off, G, bits, softmax_scale,
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        rope_cos.data_ptr(), rope_sin.data_ptr(), _stream(stream, q.device)))
+    return out
+
+
+def unpack_dequant_rope(packed, scales, group_offsets, bits, rope_cos, rope_sin, out=None, stream=None):
+    """unpack_dequant followed by the pairwise rotation of each row t by
+    rope_cos/rope_sin[t] (fp32 [>= L, D/2]): the dense post-RoPE K of a cache
+    quantized before RoPE."""
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float32, "scales")
+    if not packed.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("packed and scales must be contiguous")
+    B, H, _, L_cap = packed.shape
+    D = scales.shape[3]
+    L = int(group_offsets[-1])
+    _rope_tables(rope_cos, rope_sin, L, D)
+    if out is None:
+        out = torch.empty(B, H, L, D, dtype=torch.bfloat16, device=packed.device)
+    _need(out, torch.bfloat16, "out")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    off, G = _offsets(group_offsets)
+    _check(lib().varq_unpack_dequant_rope(
+        packed.data_ptr(), scales.data_ptr(), B, H, D, L_cap, scales.shape[2], L, off, G, bits,
+        rope_cos.data_ptr(), rope_sin.data_ptr(), out.data_ptr(), _stream(stream, packed.device)))
     return out
 
 

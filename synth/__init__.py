@@ -13,9 +13,11 @@ from .kv_synth import (  # noqa: F401
     WORKLOADS,
     frame_offsets,
     gen_next_scale_kv,
+    gen_pre_rope_frame_k,
     gen_queries,
     gen_rope_frame_k,
     gen_unit_v,
+    rope_frame_tables,
     scale_offsets,
     workload_inputs,
 )

@@ -96,6 +96,31 @@ def gen_next_scale_kv(B, H, D, offsets, n_out, seed, stream, device="cpu",
     return x.to(torch.bfloat16)
 
 
+def _frame_k_pre(B, H, D, L, gen, device, n_fast_pairs, n_out_pairs, angle_jitter):
+    """Pre-RoPE K of the next-frame generator, fp32 [B, L, H, D] (see gen_rope_frame_k)."""
+    k = torch.randn(B, L, H, D, generator=gen, device=device)
+    pairs = torch.rand(H, n_fast_pairs, generator=gen, device=device).argsort(-1)[:, :n_out_pairs]
+    amp0 = 20.0 + 30.0 * torch.rand(H, n_out_pairs, generator=gen, device=device)
+    phi0 = 2.0 * math.pi * torch.rand(H, n_out_pairs, generator=gen, device=device)
+    amp = amp0 * (1.0 + 0.1 * torch.randn(B, L, H, n_out_pairs, generator=gen, device=device))
+    ang = phi0 + angle_jitter * torch.randn(B, L, H, n_out_pairs, generator=gen, device=device)
+    ch_even = (2 * pairs)                                             # [H, P]
+    hidx = torch.arange(H, device=device)[:, None].expand_as(ch_even)
+    k[:, :, hidx, ch_even] = amp * torch.cos(ang)
+    k[:, :, hidx, ch_even + 1] = amp * torch.sin(ang)
+    return k
+
+
+def rope_frame_tables(L, D, device="cpu", frame_tokens=FRAME_TOKENS, rope_base=10000.0):
+    """RoPE along the frame axis: cos and sin of frame(t) * omega_i, omega_i =
+    base**(-2i/D), fp32 [L, D/2] each (all tokens of a frame share the angle)."""
+    frame = (torch.arange(L, device=device) // frame_tokens).to(torch.float32)   # [L]
+    i = torch.arange(D // 2, device=device, dtype=torch.float32)
+    omega = rope_base ** (-2.0 * i / D)                                           # [D/2]
+    theta = frame[:, None] * omega[None, :]                                       # [L, D/2]
+    return torch.cos(theta), torch.sin(theta)
+
+
 def gen_rope_frame_k(B, H, D, offsets, seed, stream, device="cpu", frame_tokens=FRAME_TOKENS,
                      n_fast_pairs=8, n_out_pairs=4, rope_base=10000.0, angle_jitter=0.1):
     """Post-RoPE K of a next-frame model, bf16 [B, L, H, D] (Insight 03, Eq. 3).
@@ -107,28 +132,27 @@ def gen_rope_frame_k(B, H, D, offsets, seed, stream, device="cpu", frame_tokens=
     share the angle. The frame index drives the rotation (blocks are frames)."""
     L = offsets[-1]
     gen = _gen(seed, stream, device)
-    k = torch.randn(B, L, H, D, generator=gen, device=device)
-    pairs = torch.rand(H, n_fast_pairs, generator=gen, device=device).argsort(-1)[:, :n_out_pairs]
-    amp0 = 20.0 + 30.0 * torch.rand(H, n_out_pairs, generator=gen, device=device)
-    phi0 = 2.0 * math.pi * torch.rand(H, n_out_pairs, generator=gen, device=device)
-    amp = amp0 * (1.0 + 0.1 * torch.randn(B, L, H, n_out_pairs, generator=gen, device=device))
-    ang = phi0 + angle_jitter * torch.randn(B, L, H, n_out_pairs, generator=gen, device=device)
-    ch_even = (2 * pairs)                                             # [H, P]
-    hidx = torch.arange(H, device=device)[:, None].expand_as(ch_even)
-    k[:, :, hidx, ch_even] = amp * torch.cos(ang)
-    k[:, :, hidx, ch_even + 1] = amp * torch.sin(ang)
-    # RoPE along the frame axis.
-    frame = (torch.arange(L, device=device) // frame_tokens).to(torch.float32)   # [L]
-    i = torch.arange(D // 2, device=device, dtype=torch.float32)
-    omega = rope_base ** (-2.0 * i / D)                                           # [D/2]
-    theta = frame[:, None] * omega[None, :]                                       # [L, D/2]
-    c = torch.cos(theta)[None, :, None, :]
-    s = torch.sin(theta)[None, :, None, :]
+    k = _frame_k_pre(B, H, D, L, gen, device, n_fast_pairs, n_out_pairs, angle_jitter)
+    cos, sin = rope_frame_tables(L, D, device, frame_tokens, rope_base)
+    c = cos[None, :, None, :]
+    s = sin[None, :, None, :]
     ke, ko = k[..., 0::2], k[..., 1::2]
     re = ke * c - ko * s
     ro = ke * s + ko * c
     out = torch.stack((re, ro), dim=-1).reshape(B, L, H, D)
     return out.to(torch.bfloat16)
+
+
+def gen_pre_rope_frame_k(B, H, D, offsets, seed, stream, device="cpu", frame_tokens=FRAME_TOKENS,
+                         n_fast_pairs=8, n_out_pairs=4, rope_base=10000.0, angle_jitter=0.1):
+    """The same draws as gen_rope_frame_k before the rotation: pre-RoPE K, bf16
+    [B, L, H, D], and its rotation tables (cos, sin) fp32 [L, D/2] (inputs of the
+    pre-RoPE path, project page Appendix F)."""
+    L = offsets[-1]
+    gen = _gen(seed, stream, device)
+    k = _frame_k_pre(B, H, D, L, gen, device, n_fast_pairs, n_out_pairs, angle_jitter)
+    cos, sin = rope_frame_tables(L, D, device, frame_tokens, rope_base)
+    return k.to(torch.bfloat16), cos, sin
 
 
 def gen_queries(B, Lq, H, D, seed, stream, device="cpu"):

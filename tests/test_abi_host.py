@@ -236,3 +236,17 @@ def test_frame_group_offsets(V):
     assert sizes[0] == sizes[-1] == 780 and set(sizes[1:-1]) == {1560}
     with pytest.raises(ValueError):
         V.frame_group_offsets(100, 30, phase=30)
+
+
+def test_rope_entry_validation(V):
+    import ctypes as C
+    off = (C.c_int32 * 3)(0, 5, 680)
+    ud = V.lib().varq_unpack_dequant_rope
+    # NULL table, misaligned table
+    assert ud(0x20000, 0x30000, 1, 16, 64, 680, 2, 680, off, 2, 4, None, 0x50000, 0x40000, None) == -1
+    assert ud(0x20000, 0x30000, 1, 16, 64, 680, 2, 680, off, 2, 4, 0x50002, 0x60000, 0x40000, None) == -3
+    pa = V.lib().varq_packed_attention_rope
+    args = [0x10000, 256 * 16 * 64, 16 * 64, 64, 1, 16, 64, 256, 0x20000, 0x30000, 0x40000, 0x50000,
+            680, 2, 680, off, 2, 4, 0.125, 0x60000, 256 * 16 * 64, 16 * 64, 64]
+    assert pa(*args, 0x70000, None, None) == -1
+    assert pa(*args, 0x70001, 0x80000, None) == -3

@@ -80,3 +80,25 @@ def test_generators_are_deterministic():
     assert torch.equal(a, b) and not torch.equal(a, c)
     assert a.dtype == torch.bfloat16 and a.shape == (2, off[-1], 2, 64)
     assert np.isfinite(a.float().numpy()).all()
+
+
+def test_pre_rope_generator_is_the_post_rope_one_before_rotation():
+    """gen_pre_rope_frame_k draws exactly what gen_rope_frame_k draws, before
+    the frame rotation: rotating its (bf16-rounded) K by its own tables gives the
+    post-RoPE K within the bf16 rounding of the pair (errors scale with the
+    pair's norm, since both channels of a pair mix)."""
+    import numpy as np
+    from oracle import varq_oracle as O
+    from synth import gen_pre_rope_frame_k, gen_rope_frame_k
+    from synth.kv_synth import FRAME_TOKENS
+    off = [0, FRAME_TOKENS, 2 * FRAME_TOKENS]
+    kpre, cos, sin = gen_pre_rope_frame_k(1, 2, 128, off, 0, 1)
+    kpost = gen_rope_frame_k(1, 2, 128, off, 0, 1)
+    rot = O.apply_rope(kpre.float().numpy().transpose(0, 2, 1, 3), cos.numpy(), sin.numpy()).transpose(0, 2, 1, 3)
+    ref = kpost.float().numpy()
+    pair = np.repeat(np.hypot(ref[..., 0::2], ref[..., 1::2]), 2, axis=-1)
+    assert np.all(np.abs(rot - ref) <= 2 ** -6 * pair + 2 ** -6)
+    # and the tables are the frame schedule: all tokens of a frame share the angle
+    assert np.array_equal(cos[0].numpy(), np.ones(64, np.float32))
+    assert np.array_equal(cos[FRAME_TOKENS - 1].numpy(), cos[0].numpy())
+    assert not np.array_equal(cos[FRAME_TOKENS].numpy(), cos[0].numpy())
