@@ -34,7 +34,6 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int AT_NT = 64;        // KV tokens per tile
 constexpr int AT_SL_MAXG = 32;   // blocks whose K and V scales a work-group can hold in LDS
-constexpr float AT_RESCALE_SLACK = 8.0f;   // log2 units: p <= 2^8 between rescales
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -53,18 +52,10 @@ __device__ inline float field_f32(uint32_t word, int i) {
     return (float)((int32_t)(word << (SHIFT - i * BITS)) >> SHIFT);
 }
 
-// o *= alpha on an accumulator tile that lives in AGPRs: read, scale, write
-// back in place, so the accumulators never have to move to VGPRs.
+// o *= alpha on an accumulator tile
 __device__ inline void scale_acc16(floatx16 &o, float alpha) {
-    float tmp;
-#define VARQ_SCALE_ONE(R)                                                              \
-    asm volatile("v_accvgpr_read_b32 %0, %1\n\tv_mul_f32 %0, %0, %2\n\tv_accvgpr_write_b32 %1, %0" \
-                 : "=&v"(tmp), "+a"(o[R]) : "v"(alpha));
-    VARQ_SCALE_ONE(0) VARQ_SCALE_ONE(1) VARQ_SCALE_ONE(2) VARQ_SCALE_ONE(3)
-    VARQ_SCALE_ONE(4) VARQ_SCALE_ONE(5) VARQ_SCALE_ONE(6) VARQ_SCALE_ONE(7)
-    VARQ_SCALE_ONE(8) VARQ_SCALE_ONE(9) VARQ_SCALE_ONE(10) VARQ_SCALE_ONE(11)
-    VARQ_SCALE_ONE(12) VARQ_SCALE_ONE(13) VARQ_SCALE_ONE(14) VARQ_SCALE_ONE(15)
-#undef VARQ_SCALE_ONE
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] *= alpha;
 }
 
 // BITS = 16 (DENSE): K and V are plain bf16 [B, H, rows, D] (the unfused
@@ -406,15 +397,17 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     };
 
     const float c = a.scale_log2;
-    // at head_dim 64 the 16 registers of early scores would cost the second
-    // resident workgroup per CU
-    constexpr bool EARLY_S = (D >= 128);
-
-    // one 64-token tile from LDS buffer `buf`
+    // one 64-token tile from LDS buffer `buf`. The matrix core and the vector
+    // ALUs only overlap when their instructions alternate within one wave, so
+    // the tile is issued as: scores of half 0; scores of half 1 interleaved
+    // with the exponentials of half 0; P*V of half 0 interleaved with the
+    // exponentials of half 1; P*V of half 1.
     auto compute = [&](int buf, int n0, bool masked) {
         const uint16_t *Kb = Ks + buf * KBUF + lr * KP + 8 * hf;
         const uint16_t *Vb = Vt + buf * VBUF + lr * VP + 8 * hf;
         floatx16 s[2][QB];
+        bf16x8 pop[2][QB][2];
+        float lt[2][QB];
         auto scores = [&](int tb) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
@@ -428,13 +421,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
                     s[tb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][ks], s[tb][qb], 0, 0, 0);
             }
         };
-        // EARLY_S: scores of both 32-token halves first, so that the matrix
-        // core works on the second half while the first half's softmax runs on
-        // the vector ALUs (costs 16 registers per query block)
-        if constexpr (EARLY_S) { scores(0); scores(1); }
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            if constexpr (!EARLY_S) scores(tb);
+        auto mask = [&](int tb) {
             if (masked) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -444,55 +431,125 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
                         if (tok >= L_kv) s[tb][qb][r] = -INFINITY;
                 }
             }
-            bf16x8 pop[QB][2];
+        };
+        // exponentials of half tb against the running maximum, element pairs
+        // [j0, j0 + nj) of the flattened (query block, pair) index; packed bf16
+        // p go to uu, their sum to lt
+        uint32_t uu[2][QB][8];
+        auto exps_part = [&](int tb, int j0, int nj) {
+#pragma unroll
+            for (int j = j0; j < j0 + nj; ++j) {
+                const int qb = j / 8, e = j % 8;
+                const float mneg = -m_run[qb];
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][2 * e], c, mneg));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][2 * e + 1], c, mneg));
+                uu[tb][qb][e] = pack_bf16x2(p0, p1);
+                lt[tb][qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, uu[tb][qb][e]), ones_bf16x2(),
+                                                             lt[tb][qb], false);
+            }
+        };
+        auto exps = [&](int tb, int qb) {
+            lt[tb][qb] = 0.0f;
+            exps_part(tb, 8 * qb, 8);
+        };
+        auto make_pop = [&](int tb) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    pop[tb][qb][hh] = as_bf16x8(make_uint4(uu[tb][qb][4 * hh], uu[tb][qb][4 * hh + 1],
+                                                           uu[tb][qb][4 * hh + 2], uu[tb][qb][4 * hh + 3]));
+        };
+        // The running maximum is raised only when a half's exponentials leave
+        // [0, 2^64): on the first tile (m_run = -inf gives inf or NaN) or when
+        // scores grow by more than 64 in log2 units. Below that bound p, l and
+        // o stay far from fp32 overflow, and fp32/bf16 relative precision does
+        // not depend on the offset, so no per-tile maximum is needed.
+        auto settle = [&](int tb) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                // scores are finite or -inf (masked), never NaN: the NaN-propagating
-                // maximum takes two new values per instruction and needs no quieting
-                float mx = __builtin_elementwise_maximum(s[tb][qb][0], s[tb][qb][1]);
+                if (__builtin_amdgcn_ballot_w64(!(lt[tb][qb] < 0x1p64f)) != 0) {
+                    // scores are finite or -inf (masked), never NaN
+                    float mx = __builtin_elementwise_maximum(s[tb][qb][0], s[tb][qb][1]);
 #pragma unroll
-                for (int r = 2; r < 16; r += 2)
-                    mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[tb][qb][r], s[tb][qb][r + 1]));
-                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
-                                                                 __builtin_bit_cast(uint32_t, mx), false, false);
-                // the swap returns the values of this lane's pair (lanes i and i^32)
-                mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)sw[0]),
-                                                                                     __builtin_bit_cast(float, (uint32_t)sw[1])));
-                const float mt = mx * c;
-                if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + AT_RESCALE_SLACK) != 0) {
-                    const float m_new = fmaxf(m_run[qb], mt);
+                    for (int r = 2; r < 16; r += 2)
+                        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[tb][qb][r], s[tb][qb][r + 1]));
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                                     __builtin_bit_cast(uint32_t, mx), false, false);
+                    mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)sw[0]),
+                                                                                         __builtin_bit_cast(float, (uint32_t)sw[1])));
+                    const float m_new = fmaxf(m_run[qb], mx * c);
                     const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
                     m_run[qb] = m_new;
                     l_run[qb] *= alpha;
 #pragma unroll
                     for (int d = 0; d < DBLK; ++d) scale_acc16(o[qb][d], alpha);
+                    exps(tb, qb);
                 }
-                const float mneg = -m_run[qb];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    uint32_t u[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][8 * hh + 2 * e], c, mneg));
-                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][8 * hh + 2 * e + 1], c, mneg));
-                        u[e] = pack_bf16x2(p0, p1);
-                        l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[e]), ones_bf16x2(),
-                                                                    l_run[qb], false);
-                    }
-                    pop[qb][hh] = as_bf16x8(make_uint4(u[0], u[1], u[2], u[3]));
-                }
+                l_run[qb] += lt[tb][qb];
             }
+            make_pop(tb);
+        };
+        auto kread = [&](int tb, int ks) {
+            return as_bf16x8(*reinterpret_cast<const uint4 *>(Kb + 32 * tb * KP + 16 * ks));
+        };
+        auto vread = [&](int tb, int i) {     // i = 2 * d + hh
+            return as_bf16x8(*reinterpret_cast<const uint4 *>(Vb + 32 * (i >> 1) * VP + 32 * tb + 16 * (i & 1)));
+        };
+        auto pv = [&](int tb) {
 #pragma unroll
-            for (int d = 0; d < DBLK; ++d) {
+            for (int i = 0; i < 2 * DBLK; ++i) {
+                const bf16x8 va = vread(tb, i);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const bf16x8 va = as_bf16x8(*reinterpret_cast<const uint4 *>(Vb + 32 * d * VP + 32 * tb + 16 * hh));
+                for (int qb = 0; qb < QB; ++qb)
+                    o[qb][i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[tb][qb][i & 1], o[qb][i >> 1], 0, 0, 0);
+            }
+        };
+
+        // half 0: scores
+        scores(0);
+        mask(0);
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        o[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qb][hh], o[qb][d], 0, 0, 0);
-                }
+        for (int qb = 0; qb < QB; ++qb) { lt[0][qb] = 0.0f; lt[1][qb] = 0.0f; s[1][qb] = floatx16{}; }
+        // half 1 scores on the matrix core || half 0 exponentials on the VALU;
+        // the LDS operand of step k + 1 is read during step k
+        {
+            constexpr int NS = KSTEPS;                  // matrix steps (x QB ops each)
+            constexpr int NJ = 8 * QB;                  // exponential pairs
+            bf16x8 kop[2];
+            kop[0] = kread(1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                if (k + 1 < NS) kop[(k + 1) & 1] = kread(1, k + 1);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    s[1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k & 1], qop[qb][k], s[1][qb], 0, 0, 0);
+                exps_part(0, NJ * k / NS, NJ * (k + 1) / NS - NJ * k / NS);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        settle(0);
+        mask(1);
+        // half 0 P*V on the matrix core || half 1 exponentials on the VALU
+        {
+            constexpr int NS = 2 * DBLK;
+            constexpr int NJ = 8 * QB;
+            bf16x8 vop[2];
+            vop[0] = vread(0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                if (k + 1 < NS) vop[(k + 1) & 1] = vread(0, k + 1);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    o[qb][k >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[k & 1], pop[0][qb][k & 1], o[qb][k >> 1], 0, 0, 0);
+                exps_part(1, NJ * k / NS, NJ * (k + 1) / NS - NJ * k / NS);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        settle(1);
+        pv(1);
     };
 
     // pre-RoPE: rotate the K pairs of the tile in LDS buffer `buf` (tokens past
@@ -531,12 +588,11 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
             rope_tile(cur, n0);
             lds_barrier();
         }
-        // with EARLY_S the next tile's dequantization follows this tile's
-        // compute and overlaps its last matrix ops; otherwise it goes first
-        if constexpr (EARLY_S) compute(cur, n0, false);
+        // the next tile's dequantization follows this tile's compute and
+        // overlaps its last matrix ops
+        compute(cur, n0, false);
         dequant(cur ^ 1, P0, n0 + AT_NT);
         if (jt + 2 < nt) prefetch(P0, n0 + 2 * AT_NT);
-        if constexpr (!EARLY_S) compute(cur, n0, false);
         lds_barrier();
     }
     if constexpr (ROPE) {
