@@ -119,44 +119,18 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     const int lr = lane & 31, hf = lane >> 5;
 
     for (int i = tid; i <= a.G; i += THREADS) off[i] = a.off[i];
+    // scales kept in LDS: one float4 of K and one of V per thread at most
+    // (AT_SL_MAXG * D / 4 <= THREADS), loaded now and stored once the loads
+    // below have all been waited for
+    static_assert(!SL || AT_SL_MAXG * D / 4 <= THREADS, "one scale vector per thread");
+    const bool sl_mine = SL && tid < a.G * (D / 4);
+    float4 sl_k = make_float4(0.f, 0.f, 0.f, 0.f), sl_v = sl_k;
     if constexpr (SL) {
-        const float4 *gk = reinterpret_cast<const float4 *>(a.sk + (int64_t)bh * a.G_cap * D);
-        const float4 *gv = reinterpret_cast<const float4 *>(a.sv + (int64_t)bh * a.G_cap * D);
-        float4 *lk = reinterpret_cast<float4 *>(sS);
-        float4 *lv = reinterpret_cast<float4 *>(sS + AT_SL_MAXG * D);
-        for (int i = tid; i < a.G * (D / 4); i += THREADS) { lk[i] = gk[i]; lv[i] = gv[i]; }
-    }
-
-    // Q^T operands: lane = query, slots (hf, j) = channel 16*ks + 8*hf + j
-    const int q_base = qt * QT + wave * QW + lr;
-    bf16x8 qop[QB][KSTEPS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qi = q_base + 32 * qb;
-        const uint16_t *qrow = a.q + (int64_t)b * a.sq_b + (int64_t)qi * a.sq_l + (int64_t)h * a.sq_h + 8 * hf;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (qi < a.Lq) v = *reinterpret_cast<const uint4 *>(qrow + 16 * ks);
-            qop[qb][ks] = as_bf16x8(v);
+        if (sl_mine) {
+            sl_k = reinterpret_cast<const float4 *>(a.sk + (int64_t)bh * a.G_cap * D)[tid];
+            sl_v = reinterpret_cast<const float4 *>(a.sv + (int64_t)bh * a.G_cap * D)[tid];
         }
     }
-
-    // Retire the Q loads here. Otherwise the wait-count analysis sees them
-    // pending at the loop header and waits for every outstanding load (the
-    // KV prefetch included) before the first matrix-core op of each tile.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-
-    floatx16 o[QB][DBLK];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qb][d][r] = 0.0f;
-    float m_run[QB], l_run[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.0f; }
 
     const int L_kv = (int)a.L_kv;
     const int nt = (L_kv + AT_NT - 1) / AT_NT;
@@ -199,29 +173,11 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     P0.split = false;
     int g_run = 0;    // search hint: block of the last prefetched tile
 
-    __syncthreads();   // off[] (and scales in LDS) ready
-
-    // words of tile n0 (always in bounds: t + 4 <= L_cap) and, for a tile inside
-    // one block, that block's scales
-    auto prefetch = [&](Pref &P, int n0) {
-        if constexpr (DENSE) {
-            // 4 rows of 8 channels per item; rows past L_kv re-read the last
-            // row (masked in compute): the dense buffer has exactly L_cap rows
-#pragma unroll
-            for (int r = 0; r < IPT; ++r) {
-                if (!it_ok[r]) continue;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int t = min(n0 + 4 * it_t4[r] + k, L_kv - 1);
-                    const uint4 v = *reinterpret_cast<const uint4 *>(plane[r] + (int64_t)t * (D / 2));
-                    P.wd[r][4 * k] = v.x; P.wd[r][4 * k + 1] = v.y; P.wd[r][4 * k + 2] = v.z; P.wd[r][4 * k + 3] = v.w;
-                }
-            }
-            return;
-        }
-        g_run = group_of(off, g_run, n0);
-        P.g = g_run;
-        P.split = off[g_run + 1] < min(n0 + AT_NT, L_kv);
+    // words of the (packed) tile at n0 whose first token is in block g and,
+    // when scales are not in LDS, that block's scales for the item's channels
+    auto prefetch_words = [&](Pref &P, int n0, int g, bool split) {
+        P.g = g;
+        P.split = split;
 #pragma unroll
         for (int r = 0; r < IPT; ++r) {
             if (!it_ok[r]) continue;
@@ -248,6 +204,72 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
             }
         }
     };
+
+    // words of tile n0 (always in bounds: t + 4 <= L_cap) and, for a tile inside
+    // one block, that block's scales
+    auto prefetch = [&](Pref &P, int n0) {
+        if constexpr (DENSE) {
+            // 4 rows of 8 channels per item; rows past L_kv re-read the last
+            // row (masked in compute): the dense buffer has exactly L_cap rows
+#pragma unroll
+            for (int r = 0; r < IPT; ++r) {
+                if (!it_ok[r]) continue;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int t = min(n0 + 4 * it_t4[r] + k, L_kv - 1);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(plane[r] + (int64_t)t * (D / 2));
+                    P.wd[r][4 * k] = v.x; P.wd[r][4 * k + 1] = v.y; P.wd[r][4 * k + 2] = v.z; P.wd[r][4 * k + 3] = v.w;
+                }
+            }
+            return;
+        }
+        g_run = group_of(off, g_run, n0);
+        prefetch_words(P, n0, g_run, off[g_run + 1] < min(n0 + AT_NT, L_kv));
+    };
+
+    // Tile 0's words, the queries and the LDS-bound scales are all in flight
+    // before the first wait.
+    if constexpr (!DENSE) prefetch_words(P0, 0, 0, a.off[1] < min(AT_NT, L_kv));
+
+    // Q^T operands: lane = query, slots (hf, j) = channel 16*ks + 8*hf + j
+    const int q_base = qt * QT + wave * QW + lr;
+    bf16x8 qop[QB][KSTEPS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qi = q_base + 32 * qb;
+        const uint16_t *qrow = a.q + (int64_t)b * a.sq_b + (int64_t)qi * a.sq_l + (int64_t)h * a.sq_h + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (qi < a.Lq) v = *reinterpret_cast<const uint4 *>(qrow + 16 * ks);
+            qop[qb][ks] = as_bf16x8(v);
+        }
+    }
+
+    // Retire these loads here. Otherwise the wait-count analysis sees them
+    // pending at the loop header and waits for every outstanding load (the
+    // KV prefetch included) before the first matrix-core op of each tile.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+    if constexpr (SL) {
+        if (sl_mine) {
+            reinterpret_cast<float4 *>(sS)[tid] = sl_k;
+            reinterpret_cast<float4 *>(sS + AT_SL_MAXG * D)[tid] = sl_v;
+        }
+    }
+
+    floatx16 o[QB][DBLK];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qb][d][r] = 0.0f;
+    float m_run[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.0f; }
+
+    __syncthreads();   // off[] (and scales in LDS) ready
 
     // item r of a prefetched tile into LDS buffer `buf`; scale of code i of
     // token k is sk(k, i)
@@ -300,6 +322,22 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         }
     };
 
+    // CPW scales of one block row from LDS (row = that block's D scales,
+    // offset by the item's first channel): 16-byte reads when whole words
+    // tile the row, the channel past the row's end clamped otherwise
+    auto scale_row = [&](float (&dst)[CPW], const float *row, int ncw) {
+        if constexpr (D % CPW == 0 && CPW % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CPW; i += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(row + i);
+                dst[i] = v.x; dst[i + 1] = v.y; dst[i + 2] = v.z; dst[i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) dst[i] = row[min(i, ncw - 1)];
+        }
+    };
+
     // dequantize a prefetched tile starting at token n0 into LDS buffer `buf`
     auto dequant = [&](int buf, const Pref &P, int n0) {
         if constexpr (DENSE) {
@@ -339,8 +377,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
                 const float *base = sS + (it_v[r] ? AT_SL_MAXG * D : 0) + cbase;
                 if (!P.split) {
                     float scl[CPW];
-#pragma unroll
-                    for (int i = 0; i < CPW; ++i) scl[i] = base[P.g * D + min(i, ncw - 1)];
+                    scale_row(scl, base + P.g * D, ncw);
                     dequant_item(buf, P, r, [&](int, int i) { return scl[i]; });
                 } else {
                     // a tile with a block boundary: each token takes the scale
@@ -354,8 +391,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
                             g = group_of(off, g, min(t0 + k, L_kv - 1));
-#pragma unroll
-                            for (int i = 0; i < CPW; ++i) scl[k][i] = base[g * D + min(i, ncw - 1)];
+                            scale_row(scl[k], base + g * D, ncw);
                         }
                         dequant_item(buf, P, r, [&](int k, int i) { return scl[k][i]; });
                     } else {
@@ -577,7 +613,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     // rotated in place (one more barrier) before its compute.
     auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
     int jt = 0;
-    prefetch(P0, 0);
+    if constexpr (DENSE) prefetch(P0, 0);
     dequant(0, P0, 0);
     if (nt > 1) prefetch(P0, AT_NT);
     lds_barrier();
