@@ -2,8 +2,9 @@
 """Benchmark of the VAR-Q packed KV-cache hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-quantize+pack of K and V (per-channel x per-block absmax, scales, codes, INT32
-words into a preallocated cache) followed by the packed-KV attention call(s)
+quantize+pack of K and V in one call (per-channel x per-block absmax, scales,
+codes, INT32 words into a preallocated cache) followed by the packed-KV
+attention call(s)
 of the workload (load packed words, unpack, dequantize, QK^T, softmax, PV).
 For a next-frame workload the step is the whole block loop: quantize block j,
 then block j's queries attend to blocks 0..j.
@@ -13,7 +14,7 @@ bf16 in + words + scales out; attention: Q + O + packed K/V + scales) divided
 by the step time, in GB/s. `roofline` reports the kernel with the largest
 share of the step time against its bound (HBM for quant-pack, bf16 MFMA for
 attention); its duration comes from HIP events recorded around each launch on
-the launch stream during the timed steps. `cpu_baseline` times the CPU oracle
+the launch stream in a second pass of the timed steps. `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload.
 """
 
@@ -367,7 +368,7 @@ def main():
         if st[0] == "qp":
             _, t0, t1, g0, g1 = st
             b1 = qp_bytes(B, t1 - t0, H, D, g1 - g0, bits)
-            qp_b += [b1, b1]
+            qp_b.append(2 * b1)                 # K and V in one launch
             step_bytes += 2 * b1
         else:
             _, q0, ql, L_kv, g1 = st
@@ -377,7 +378,7 @@ def main():
             step_bytes += b1
 
     # one event pair per launch of every timed step, created before timing
-    n_qp_launches = sum(2 for st in launches if st[0] == "qp")
+    n_qp_launches = sum(1 for st in launches if st[0] == "qp")
     n_at_launches = sum(1 for st in launches if st[0] != "qp")
 
     def event_pairs(n):
@@ -401,9 +402,8 @@ def main():
             if st[0] == "qp":
                 _, t0, t1, g0, g1 = st
                 rel = [o - t0 for o in off[g0:g1 + 1]]
-                for x, p, s in ((k, pk, sk), (v, pv, sv)):
-                    timed("qp", record, lambda: varq.quantize_pack(x[:, t0:t1], rel, bits, p, s,
-                                                                   tok_start=t0, group_start=g0))
+                timed("qp", record, lambda: varq.quantize_pack_kv(k[:, t0:t1], v[:, t0:t1], rel, bits, pk, sk, pv, sv,
+                                                                  tok_start=t0, group_start=g0))
             else:
                 _, q0, ql, L_kv, g1 = st
                 timed("attn", record, lambda: varq.packed_attention(q, pk, sk, pv, sv, off[:g1 + 1], bits, out=out))

@@ -113,6 +113,26 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
                        void *stream);
 
 /*
+ * quantize+pack of K and V together (project page Fig. 8: the new block's K
+ * and V are both quantized and packed before attention reads them back): the
+ * same result as varq_quantize_pack(k -> packed_k, scales_k) followed by
+ * varq_quantize_pack(v -> packed_v, scales_v), with one shape, block map and
+ * cache layout for both. k and v have strides of their own; packed_k/packed_v
+ * and scales_k/scales_v are distinct buffers. When every block fits one
+ * work-group's 16384 elements both tensors go through one launch; otherwise
+ * the cooperative kernel runs once per tensor (same scratch rules as above).
+ * Errors: those of varq_quantize_pack, for either tensor, and VARQ_EINVAL when
+ * K and V share a cache buffer.
+ */
+int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_h,
+                          const void *v, int64_t sv_b, int64_t sv_l, int64_t sv_h,
+                          int B, int H, int D, int64_t L_in,
+                          const int32_t *group_offsets, int G_in, int bits,
+                          int32_t *packed_k, float *scales_k, int32_t *packed_v, float *scales_v,
+                          int64_t L_cap, int64_t tok_start, int64_t G_cap, int64_t group_start,
+                          void *stream);
+
+/*
  * Pre-RoPE quantization (project page Appendix F / Table 7; Insight 03, Eq. 3):
  * the cache holds K quantized BEFORE the rotary embedding, and the rotation is
  * applied to the dequantized K. The schedule is a pair of fp32 tables

@@ -21,6 +21,7 @@ from .varq import (  # noqa: F401
     packed_attention_rope,
     quantize_pack,
     quantize_pack_grouped,
+    quantize_pack_kv,
     unpack_dequant,
     unpack_dequant_rope,
     words_per_row,

@@ -55,7 +55,8 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Wave-uniform description of a unit.
 struct Unit {
-    int64_t id, bh;
+    int64_t id, bh;      // id within its tensor
+    int t;               // tensor: 0 = x, 1 = x2 (one launch for K and V)
     int g0, nb;          // first block, number of blocks (> 1 only for packs)
     int c, nc;           // chunk index and chunk count of block g0 (nc == 1 for packs)
     int row0, n;         // first row relative to x, rows
@@ -80,6 +81,8 @@ __device__ inline int lds_uniform(const int32_t *p) { return __builtin_amdgcn_re
 
 __device__ inline Unit unit_of(const QuantPackArgs &a, const Tables &tb, int64_t id) {
     Unit U;
+    U.t = id >= a.n_units_one;
+    if (U.t) id -= a.n_units_one;
     U.id = id;
     U.bh = id / a.units_per_bh;
     const int r_in = (int)(id - U.bh * a.units_per_bh);
@@ -173,8 +176,10 @@ struct Lane {
 // lane offset (the host checks that a unit's rows span < 2^31 bytes).
 __device__ inline void load_unit(const QuantPackArgs &a, const Unit &U, uint4 (&v)[QP_ITEMS], const Lane &L) {
     const int64_t b = U.bh / a.H, h = U.bh - b * a.H;
-    const char *ubase = reinterpret_cast<const char *>(a.x + b * a.sx_b + h * a.sx_h + (int64_t)U.row0 * a.sx_l);
-    const uint32_t row_bytes = (uint32_t)a.sx_l * 2u;
+    const uint16_t *x = U.t ? a.x2 : a.x;
+    const int64_t sb = U.t ? a.sx2_b : a.sx_b, sl = U.t ? a.sx2_l : a.sx_l, sh = U.t ? a.sx2_h : a.sx_h;
+    const char *ubase = reinterpret_cast<const char *>(x + b * sb + h * sh + (int64_t)U.row0 * sl);
+    const uint32_t row_bytes = (uint32_t)sl * 2u;
 #pragma unroll
     for (int k = 0; k < QP_ITEMS; ++k) {
         const int r = min(L.rr * QP_ITEMS + k, U.n - 1);
@@ -185,7 +190,7 @@ __device__ inline void load_unit(const QuantPackArgs &a, const Unit &U, uint4 (&
 // Word plane p, unit row r of unit U: wave-uniform base plus a 32-bit lane
 // offset (the host checks that W * L_cap words span < 2^31 bytes).
 __device__ inline uint32_t *word_at(const QuantPackArgs &a, const Unit &U, int p, int r) {
-    char *base = reinterpret_cast<char *>(a.packed + U.bh * a.W * a.L_cap + a.tok_start + U.row0);
+    char *base = reinterpret_cast<char *>((U.t ? a.packed2 : a.packed) + U.bh * a.W * a.L_cap + a.tok_start + U.row0);
     return reinterpret_cast<uint32_t *>(base + (uint32_t)(p * (uint32_t)a.L_cap + r) * 4u);
 }
 
@@ -534,7 +539,7 @@ __device__ inline float put_scale(float *sh_s, float *sh_y, int slot, int D, int
 }
 
 __device__ inline float *scale_ptr(const QuantPackArgs &a, const Unit &U, int tid) {
-    return a.scales + (U.bh * a.G_cap + a.group_start + U.g0) * a.D + tid;
+    return (U.t ? a.scales2 : a.scales) + (U.bh * a.G_cap + a.group_start + U.g0) * a.D + tid;
 }
 
 template <int N>

@@ -125,39 +125,23 @@ int scratch_for(hipStream_t st, size_t n_slots, uint32_t **sync, uint64_t **slot
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int varq_codes_per_word(int bits) { return (bits >= 2 && bits <= 8) ? 32 / bits : 0; }
-
-int varq_words_per_row(int head_dim, int bits) {
-    if (bits < 2 || bits > 8 || head_dim < 1) return 0;
-    return words_per_row(head_dim, bits);
-}
-
-int varq_cache_bytes(int B, int H, int head_dim, int64_t L_cap, int64_t G_cap, int bits,
-                     int64_t *packed_bytes, int64_t *scale_bytes) {
-    if (int r = check_bits(bits)) return r;
-    if (B < 1 || H < 1 || head_dim < 1 || L_cap < 0 || G_cap < 0)
-        return fail(VARQ_EINVAL, "cache_bytes: sizes must be positive (B=%d H=%d D=%d L_cap=%lld G_cap=%lld)",
-                    B, H, head_dim, (long long)L_cap, (long long)G_cap);
-    const int64_t W = words_per_row(head_dim, bits);
-    if (packed_bytes) *packed_bytes = (int64_t)B * H * W * L_cap * 4;
-    if (scale_bytes) *scale_bytes = (int64_t)B * H * G_cap * head_dim * 4;
-    return ok();
-}
-
-int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
-                       int B, int H, int D, int64_t L_in,
-                       const int32_t *group_offsets, int G_in, int bits,
-                       int32_t *packed, int64_t L_cap, int64_t tok_start,
-                       float *scales, int64_t G_cap, int64_t group_start,
-                       void *stream) {
+// Validates one tensor's quantize+pack arguments and fills the launch
+// arguments; *empty is set when there is nothing to write.
+int qp_setup(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
+             int B, int H, int D, int64_t L_in,
+             const int32_t *group_offsets, int G_in, int bits,
+             int32_t *packed, int64_t L_cap, int64_t tok_start,
+             float *scales, int64_t G_cap, int64_t group_start,
+             varq::QuantPackArgs &a, bool *empty, bool *split, int *max_chunks) {
+    *empty = false;
     if (int r = check_bits(bits)) return r;
     if (B < 1 || H < 1) return fail(VARQ_EINVAL, "quantize_pack: B=%d H=%d must be >= 1", B, H);
     if (D < 8 || D > 256 || D % 8 != 0)
         return fail(VARQ_EINVAL, "quantize_pack: head_dim %d must be a multiple of 8 in 8..256", D);
     if (L_in < 0) return fail(VARQ_EINVAL, "quantize_pack: L_in=%lld < 0", (long long)L_in);
-    if (L_in == 0 && G_in == 0) return ok();                       // nothing to write
+    if (L_in == 0 && G_in == 0) { *empty = true; return ok(); }    // nothing to write
     if (int r = check_offsets(group_offsets, G_in, L_in, "quantize_pack")) return r;
     if (!x || !packed || !scales) return fail(VARQ_EINVAL, "quantize_pack: NULL tensor pointer");
     if (!aligned(x, 16) || sx_b % 8 || sx_l % 8 || sx_h % 8)
@@ -171,7 +155,6 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
                     (long long)tok_start, (long long)(tok_start + L_in), (long long)group_start,
                     (long long)(group_start + G_in), (long long)L_cap, (long long)G_cap);
 
-    varq::QuantPackArgs a;
     std::memset(&a, 0, sizeof(a));
     a.x = static_cast<const uint16_t *>(x);
     a.sx_b = sx_b; a.sx_l = sx_l; a.sx_h = sx_h;
@@ -222,7 +205,9 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
     a.unit_start[G_in] = units;
     a.units_per_bh = units;
     a.n_units = (int64_t)B * H * units;
-    const bool split = max_nc > 1;
+    a.n_units_one = a.n_units;
+    *split = max_nc > 1;
+    *max_chunks = max_nc;
 
     // LDS regions (bytes, 16-aligned): block maxima [max_pack][D], scales and
     // reciprocals [max_pack + 2][D], the staging area for words or code rows
@@ -241,6 +226,13 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
         a.lds_us = o;    o += up16((int64_t)(G_in + 1) * 4);
         a.lds_bytes = o;
     }
+    return VARQ_OK;
+}
+
+// Launches a prepared quantize+pack (one tensor, or two whose units follow
+// each other in one non-split launch).
+int qp_launch(varq::QuantPackArgs &a, int bits, bool split, int max_nc, void *stream) {
+    const int D = a.D;
     int grid = 0;
     if (split) {
         const int resident = varq::quant_pack_resident_blocks(bits, a.lds_bytes);
@@ -251,7 +243,7 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
         if (max_nc > grid)
             return fail(VARQ_EUNSUPPORTED, "quantize_pack: a block of %d chunks exceeds the %d resident work-groups",
                         max_nc, grid);
-        const size_t bhg = (size_t)B * H * G_in;
+        const size_t bhg = (size_t)a.B * a.H * a.G;
         uint32_t *sync = nullptr;
         uint64_t *slots = nullptr;
         if (int r = scratch_for(static_cast<hipStream_t>(stream), ((size_t)a.n_units + bhg) * D, &sync, &slots))
@@ -265,6 +257,78 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
     }
     return launch_status(varq::launch_quant_pack(a, bits, grid, split, static_cast<hipStream_t>(stream)),
                          "quantize_pack");
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int varq_codes_per_word(int bits) { return (bits >= 2 && bits <= 8) ? 32 / bits : 0; }
+
+int varq_words_per_row(int head_dim, int bits) {
+    if (bits < 2 || bits > 8 || head_dim < 1) return 0;
+    return words_per_row(head_dim, bits);
+}
+
+int varq_cache_bytes(int B, int H, int head_dim, int64_t L_cap, int64_t G_cap, int bits,
+                     int64_t *packed_bytes, int64_t *scale_bytes) {
+    if (int r = check_bits(bits)) return r;
+    if (B < 1 || H < 1 || head_dim < 1 || L_cap < 0 || G_cap < 0)
+        return fail(VARQ_EINVAL, "cache_bytes: sizes must be positive (B=%d H=%d D=%d L_cap=%lld G_cap=%lld)",
+                    B, H, head_dim, (long long)L_cap, (long long)G_cap);
+    const int64_t W = words_per_row(head_dim, bits);
+    if (packed_bytes) *packed_bytes = (int64_t)B * H * W * L_cap * 4;
+    if (scale_bytes) *scale_bytes = (int64_t)B * H * G_cap * head_dim * 4;
+    return ok();
+}
+
+int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
+                       int B, int H, int D, int64_t L_in,
+                       const int32_t *group_offsets, int G_in, int bits,
+                       int32_t *packed, int64_t L_cap, int64_t tok_start,
+                       float *scales, int64_t G_cap, int64_t group_start,
+                       void *stream) {
+    varq::QuantPackArgs a;
+    bool empty = false, split = false;
+    int max_nc = 1;
+    if (int r = qp_setup(x, sx_b, sx_l, sx_h, B, H, D, L_in, group_offsets, G_in, bits, packed, L_cap, tok_start,
+                         scales, G_cap, group_start, a, &empty, &split, &max_nc))
+        return r;
+    if (empty) return ok();
+    return qp_launch(a, bits, split, max_nc, stream);
+}
+
+int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_h,
+                          const void *v, int64_t sv_b, int64_t sv_l, int64_t sv_h,
+                          int B, int H, int D, int64_t L_in,
+                          const int32_t *group_offsets, int G_in, int bits,
+                          int32_t *packed_k, float *scales_k, int32_t *packed_v, float *scales_v,
+                          int64_t L_cap, int64_t tok_start, int64_t G_cap, int64_t group_start,
+                          void *stream) {
+    varq::QuantPackArgs a, av;
+    bool empty = false, split = false;
+    int max_nc = 1;
+    if (int r = qp_setup(k, sk_b, sk_l, sk_h, B, H, D, L_in, group_offsets, G_in, bits, packed_k, L_cap, tok_start,
+                         scales_k, G_cap, group_start, a, &empty, &split, &max_nc))
+        return r;
+    if (int r = qp_setup(v, sv_b, sv_l, sv_h, B, H, D, L_in, group_offsets, G_in, bits, packed_v, L_cap, tok_start,
+                         scales_v, G_cap, group_start, av, &empty, &split, &max_nc))
+        return r;
+    if (empty) return ok();
+    if (packed_k == packed_v || scales_k == scales_v)
+        return fail(VARQ_EINVAL, "quantize_pack_kv: K and V need caches of their own");
+    if (split) {
+        // blocks longer than one unit: the cooperative kernel, once per tensor
+        if (int r = qp_launch(a, bits, split, max_nc, stream)) return r;
+        return qp_launch(av, bits, split, max_nc, stream);
+    }
+    a.x2 = av.x;
+    a.sx2_b = av.sx_b; a.sx2_l = av.sx_l; a.sx2_h = av.sx_h;
+    a.packed2 = av.packed;
+    a.scales2 = av.scales;
+    a.n_units = 2 * a.n_units_one;
+    return qp_launch(a, bits, split, max_nc, stream);
 }
 
 int64_t varq_grouped_scale_count(int mode, int B, int64_t L, int H, int D, int G) {

@@ -26,6 +26,13 @@ struct QuantPackArgs {
     int64_t sx_b, sx_l, sx_h;
     uint32_t *packed;           // [B, H, W, L_cap]
     float *scales;              // [B, H, G_cap, D]
+    // a second tensor of the same shape, block map and cache layout (V next
+    // to K): units [n_units_one, n_units) are its units (non-split launches)
+    const uint16_t *x2;
+    int64_t sx2_b, sx2_l, sx2_h;
+    uint32_t *packed2;
+    float *scales2;
+    int64_t n_units_one;        // units of one tensor (n_units when x2 is null)
     uint64_t *part;             // [n_units, D]
     uint64_t *fin;              // [B*H*G, D]
     uint32_t *sync;             // [3]

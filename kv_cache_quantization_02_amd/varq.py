@@ -38,6 +38,8 @@ _SIGNATURES = {
     "varq_cache_bytes": (_i32, [_i32, _i32, _i32, _i64, _i64, _i32, _i64p, _i64p]),
     "varq_quantize_pack": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i32p, _i32, _i32,
                                   _vp, _i64, _i64, _vp, _i64, _i64, _vp]),
+    "varq_quantize_pack_kv": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64,
+                                     _i32p, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]),
     "varq_packed_attention": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64,
                                      _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32p, _i32, _i32,
                                      _f32, _vp, _i64, _i64, _i64, _vp]),
@@ -159,6 +161,33 @@ def quantize_pack(x, group_offsets, bits, packed, scales, tok_start=0, group_sta
         packed.data_ptr(), packed.shape[3], tok_start, scales.data_ptr(), scales.shape[2],
         group_start, _stream(stream, x.device)))
     return packed, scales
+
+
+def quantize_pack_kv(k, v, group_offsets, bits, packed_k, scales_k, packed_v, scales_v,
+                     tok_start=0, group_start=0, stream=None):
+    """quantize_pack of k and of v (same shape and block map, each bf16
+    [B, L_in, H, D] with its own strides) into their own caches, in one launch
+    when every block fits one work-group."""
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{n} must be [B, L, H, D] with channel stride 1")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have one shape")
+    for t, dt, n in ((packed_k, torch.int32, "packed_k"), (packed_v, torch.int32, "packed_v"),
+                     (scales_k, torch.float32, "scales_k"), (scales_v, torch.float32, "scales_v")):
+        _need(t, dt, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if packed_k.shape != packed_v.shape or scales_k.shape != scales_v.shape:
+        raise ValueError("K and V caches must have one layout")
+    B, L, H, D = k.shape
+    off, G = _offsets(group_offsets)
+    _check(lib().varq_quantize_pack_kv(
+        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2), v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
+        B, H, D, L, off, G, bits, packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
+        packed_k.shape[3], tok_start, scales_k.shape[2], group_start, _stream(stream, k.device)))
+    return packed_k, scales_k, packed_v, scales_v
 
 
 def frame_group_offsets(L, group_tokens, phase=0):

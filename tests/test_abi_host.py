@@ -100,6 +100,34 @@ def test_quantize_pack_validation(V):
     assert _qp(V, bits=9) == -2 and "bits" in V.last_error()
 
 
+def _qpkv(V, **kw):
+    """Call varq_quantize_pack_kv with defaults overridden by kw; returns the status."""
+    a = dict(k=0x10000, sk_b=680 * 16 * 64, sk_l=16 * 64, sk_h=64, v=0x70000, sv_b=680 * 16 * 64, sv_l=16 * 64,
+             sv_h=64, B=1, H=16, D=64, L_in=680, off=[0, 1, 5, 680], bits=4, packed_k=0x20000, scales_k=0x30000,
+             packed_v=0x40000, scales_v=0x50000, L_cap=680, tok_start=0, G_cap=3, group_start=0)
+    a.update(kw)
+    off = (ctypes.c_int32 * len(a["off"]))(*a["off"])
+    return V.lib().varq_quantize_pack_kv(
+        a["k"], a["sk_b"], a["sk_l"], a["sk_h"], a["v"], a["sv_b"], a["sv_l"], a["sv_h"], a["B"], a["H"], a["D"],
+        a["L_in"], off, len(a["off"]) - 1, a["bits"], a["packed_k"], a["scales_k"], a["packed_v"], a["scales_v"],
+        a["L_cap"], a["tok_start"], a["G_cap"], a["group_start"], None)
+
+
+def test_quantize_pack_kv_validation(V):
+    """Each tensor is validated as by varq_quantize_pack; K and V may not share a buffer."""
+    assert _qpkv(V, bits=9) == -2
+    assert _qpkv(V, off=[0, 5, 5, 680]) == -1
+    assert _qpkv(V, k=0) == -1 and _qpkv(V, v=0) == -1
+    assert _qpkv(V, packed_v=0) == -1 and _qpkv(V, scales_v=0) == -1
+    assert _qpkv(V, v=0x70008) == -3 and _qpkv(V, sv_l=16 * 64 + 4) == -3
+    assert _qpkv(V, k=0x10008) == -3
+    assert _qpkv(V, packed_v=0x40004) == -3
+    assert _qpkv(V, L_cap=672) == -4 and _qpkv(V, G_cap=2) == -4
+    assert _qpkv(V, packed_v=0x20000) == -1 and "own" in V.last_error()
+    assert _qpkv(V, scales_v=0x30000) == -1
+    assert _qpkv(V, L_in=0, off=[0]) == 0                       # empty input: nothing to do
+
+
 def _attn(V, **kw):
     a = dict(q=0x10000, sq_b=256 * 16 * 64, sq_l=16 * 64, sq_h=64, B=1, H=16, D=64, Lq=256,
              pk=0x20000, sk=0x30000, pv=0x40000, sv=0x50000, L_cap=680, G_cap=10, L_kv=680,

@@ -1,0 +1,123 @@
+"""GPU parity of varq_quantize_pack_kv (K and V quantized and packed by one
+call) against the oracle's quantize_pack of each tensor: words and scales
+bit-exact, nothing written outside the addressed rows and block slots."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import varq_oracle as O
+from synth import WORKLOADS, gen_next_scale_kv, gen_rope_frame_k, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def V():
+    from kv_cache_quantization_02_amd import varq
+    varq.lib()
+    return varq
+
+
+def _caches(V, B, H, D, L_cap, G_cap, bits):
+    W = V.words_per_row(D, bits)
+    L_cap = V.round_capacity(L_cap)
+    pk = torch.full((B, H, W, L_cap), -1, dtype=torch.int32, device=DEV)      # sentinels
+    pv = torch.full_like(pk, -1)
+    sk = torch.full((B, H, G_cap, D), -1.0, dtype=torch.float32, device=DEV)
+    sv = torch.full_like(sk, -1.0)
+    return pk, sk, pv, sv
+
+
+def _check(V, k_cpu, v_cpu, off, bits, k_dev=None, v_dev=None, tok_start=0, group_start=0, extra_rows=0,
+           extra_groups=0):
+    B, L, H, D = k_cpu.shape
+    G = len(off) - 1
+    pk, sk, pv, sv = _caches(V, B, H, D, tok_start + L + extra_rows, group_start + G + extra_groups, bits)
+    V.quantize_pack_kv(k_cpu.to(DEV) if k_dev is None else k_dev, v_cpu.to(DEV) if v_dev is None else v_dev,
+                       off, bits, pk, sk, pv, sv, tok_start=tok_start, group_start=group_start)
+    torch.cuda.synchronize()
+    for name, x, p, s in (("K", k_cpu, pk, sk), ("V", v_cpu, pv, sv)):
+        w_ref, s_ref = O.quantize_pack(x.float().numpy(), off, bits)
+        w = p.cpu().numpy().view(np.uint32)
+        sc = s.cpu().numpy().view(np.uint32)
+        assert np.array_equal(w[..., tok_start:tok_start + L], w_ref), (name, bits, "words")
+        assert np.array_equal(sc[:, :, group_start:group_start + G], s_ref.view(np.uint32)), (name, bits, "scales")
+        assert (w[..., :tok_start] == 0xFFFFFFFF).all() and (w[..., tok_start + L:] == 0xFFFFFFFF).all(), \
+            (name, "rows outside the call written")
+        assert (sc[:, :, :group_start] == np.float32(-1).view(np.uint32)).all(), (name, "slots before written")
+        assert (sc[:, :, group_start + G:] == np.float32(-1).view(np.uint32)).all(), (name, "slots after written")
+    return pk, sk, pv, sv
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_kv_small_all_bits(V, bits):
+    # head_dim 40 (five 8-channel chunks) and blocks of 1 to 16 tokens
+    _say(f"[kv small b{bits}]")
+    g = torch.Generator().manual_seed(200 + bits)
+    B, L, H, D = 2, 37, 3, 40
+    k = (torch.randn(B, L, H, D, generator=g) * 3).to(torch.bfloat16)
+    v = (torch.randn(B, L, H, D, generator=g) * 0.5).to(torch.bfloat16)
+    v[0, 14:30, 1] = 0                                   # an all-zero block of one head
+    _check(V, k, v, [0, 1, 5, 14, 30, 37], bits, extra_rows=11, extra_groups=2)
+
+
+def test_kv_placement_and_strides(V):
+    """Rows and block slots at an offset of a larger cache; V a strided view."""
+    _say("[kv placement]")
+    g = torch.Generator().manual_seed(5)
+    B, L, H, D = 3, 50, 4, 64
+    k = torch.randn(B, L, H, D, generator=g).to(torch.bfloat16)
+    big = torch.randn(B, L + 9, H + 2, D, generator=g).to(torch.bfloat16)
+    v_view = big.to(DEV)[:, 4:4 + L, 1:1 + H]
+    _check(V, k, v_view.cpu().contiguous(), [0, 9, 25, 50], 4, v_dev=v_view, tok_start=16, group_start=2,
+           extra_rows=8, extra_groups=1)
+
+
+def test_kv_split_blocks(V):
+    """Blocks longer than one work-group's rows (head_dim 128: 128 rows) take the
+    cooperative kernel, once per tensor."""
+    _say("[kv split]")
+    g = torch.Generator().manual_seed(6)
+    B, L, H, D = 1, 700, 3, 128
+    k = (torch.randn(B, L, H, D, generator=g) * 2).to(torch.bfloat16)
+    v = torch.randn(B, L, H, D, generator=g).to(torch.bfloat16)
+    _check(V, k, v, [0, 4, 300, 700], 4)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_kv_var_d30_full(V, bits):
+    """The VAR-d30-like K and V caches at full size (16 x 680 tokens x 30 heads x 64)."""
+    _say(f"[kv var_d30 b{bits}]")
+    wl = WORKLOADS["var_d30"]
+    k, v, _ = workload_inputs(wl, seed=0)
+    _check(V, k, v, list(wl.offsets), bits)
+
+
+def test_kv_equals_two_calls_on_a_long_cache(V):
+    """Next-frame K/V (1560-token frames): the fused call writes exactly what two
+    quantize_pack calls write."""
+    _say("[kv self_forcing]")
+    wl = WORKLOADS["self_forcing"]
+    off = list(wl.offsets)[:7]
+    L = off[-1]
+    B, H, D = 2, wl.H, wl.D
+    k = gen_rope_frame_k(B, H, D, off, 0, 1, DEV, n_out_pairs=wl.n_out_k)
+    v = gen_next_scale_kv(B, H, D, off, wl.n_out_v, 0, 2, DEV, shared_across_batch=False)
+    pk, sk, pv, sv = _caches(V, B, H, D, L, len(off) - 1, 4)
+    V.quantize_pack_kv(k, v, off, 4, pk, sk, pv, sv)
+    qk, tk, qv, tv = _caches(V, B, H, D, L, len(off) - 1, 4)
+    V.quantize_pack(k, off, 4, qk, tk)
+    V.quantize_pack(v, off, 4, qv, tv)
+    torch.cuda.synchronize()
+    for a, b in ((pk, qk), (pv, qv), (sk.view(torch.int32), tk.view(torch.int32)),
+                 (sv.view(torch.int32), tv.view(torch.int32))):
+        assert torch.equal(a, b)
