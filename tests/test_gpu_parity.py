@@ -336,6 +336,29 @@ def test_attention_ragged_and_short_windows(V):
             _assert_attn(_gpu_rows(out), ob, C, literal=True, tag=f"L={L} Lq={Lq} D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_attention_running_maximum_jumps(V, D, bits):
+    """Scores that jump by far more than 64 in log2 units in a later block (the
+    running maximum is raised and the half-tile recomputed), grow block by
+    block, or start large and fall far below (later exponentials underflow)."""
+    g = torch.Generator().manual_seed(11 + D + bits)
+    B, H, L, Lq = 2, 3, 680, 100
+    off = [0, 64, 200, 330, 450, 680]       # blocks over several tiles, boundaries inside tiles
+    base = torch.randn(B, L, H, D, generator=g)
+    q = torch.randn(B, Lq, H, D, generator=g).to(torch.bfloat16)
+    v = (torch.randn(B, L, H, D, generator=g) * 2).to(torch.bfloat16)
+    for name, f in (("jump", (1, 1, 40, 1, 80)), ("grow", (1, 3, 9, 27, 81)), ("fall", (80, 1, 1, 1, 0.01))):
+        _say(f"[attn running max {name} D={D} bits={bits}]")
+        k = base.clone()
+        for j in range(len(off) - 1):
+            k[:, off[j]:off[j + 1]] *= f[j]
+        k = k.to(torch.bfloat16)
+        out, _ = _gpu_attention(V, k.to(DEV), v.to(DEV), q.to(DEV), off, bits)
+        _, C, ob = _oracle_attention(k, v, q, off, bits)
+        _assert_attn(_gpu_rows(out), ob, C, tag=f"{name} D={D} bits={bits}")
+
+
 def test_attention_strided_q_out(V):
     _say("[attn strided q/out]")
     g = torch.Generator().manual_seed(4)
