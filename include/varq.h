@@ -240,6 +240,15 @@ int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_
  *               strides multiples of 4. Must not overlap q or the cache.
  * Errors: VARQ_EBITS, VARQ_EINVAL, VARQ_EALIGN, VARQ_ECAPACITY, VARQ_EUNSUPPORTED
  * (D not 64/128), VARQ_ELAUNCH.
+ * Scratch: when (b, h, query tile) work-groups fill less than two rounds of the
+ * device, the window's 64-token tiles run in up to 8 ranges (at least 8 tiles
+ * each) and a second kernel merges the ranges' unnormalized outputs and
+ * (maximum, sum) pairs with log-sum-exp weights. The partials, S*B*H*Lq*(D+2)
+ * fp32 for S ranges, live in device scratch the library owns per (device,
+ * stream), grown on demand with hipMalloc (after synchronizing that stream)
+ * and kept until the process ends. Calls on one stream are ordered; calls on
+ * different streams use different scratch. The range count depends only on
+ * the shapes and the device's compute-unit count.
  */
 int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
                           int B, int H, int D, int64_t Lq,
@@ -284,6 +293,8 @@ int varq_unpack_dequant(const int32_t *packed, const float *scales,
  *               strides multiples of 4. Must not overlap q, k or v.
  * Errors: VARQ_EINVAL, VARQ_EALIGN, VARQ_ECAPACITY (L_kv > L_rows),
  * VARQ_EUNSUPPORTED (D not 64/128), VARQ_ELAUNCH.
+ * Scratch and KV ranges as for varq_packed_attention (same plan for the same
+ * shapes, so both paths compute in the same order).
  */
 int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
                         int B, int H, int D, int64_t Lq,

@@ -107,11 +107,14 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     __shared__ int32_t off[VARQ_MAX_GROUPS_DEV + 1];
     __shared__ __attribute__((aligned(16))) float sS[SL ? 2 * AT_SL_MAXG * D : 4];   // K rows, then V rows
 
-    const int n_blocks = a.n_qtiles * a.B * a.H;
+    const int n_blocks = a.n_qtiles * a.B * a.H * a.kv_splits;
     const int lid = (int)xcd_logical_id(blockIdx.x, n_blocks);
     if (lid < 0) return;
+    // logical id = ((b*H + h) * kv_splits + split) * n_qtiles + q-tile: the
+    // q-tiles of one KV range run on one XCD and share its L2
     const int qt = lid % a.n_qtiles;
-    const int bh = lid / a.n_qtiles;
+    const int split = (lid / a.n_qtiles) % a.kv_splits;
+    const int bh = lid / a.n_qtiles / a.kv_splits;
     const int b = bh / a.H, h = bh % a.H;
 
     const int tid = threadIdx.x;
@@ -134,6 +137,9 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
 
     const int L_kv = (int)a.L_kv;
     const int nt = (L_kv + AT_NT - 1) / AT_NT;
+    // this work-group's KV tiles [t_begin, t_end)
+    const int t_begin = a.split_t0[split], t_end = a.split_t0[split + 1];
+    const int n_begin = t_begin * AT_NT, g_begin = a.split_g0[split];
 
     // ---------------- items of 4 tokens: K items plane-fastest, V items
     // token-fastest, which makes both LDS write patterns bank-conflict free
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     Pref P0;
     P0.g = 0;
     P0.split = false;
-    int g_run = 0;    // search hint: block of the last prefetched tile
+    int g_run = a.split_g0[split];    // search hint: block of the last prefetched tile
 
     // words of the (packed) tile at n0 whose first token is in block g and,
     // when scales are not in LDS, that block's scales for the item's channels
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
 
     // Tile 0's words, the queries and the LDS-bound scales are all in flight
     // before the first wait.
-    if constexpr (!DENSE) prefetch_words(P0, 0, 0, a.off[1] < min(AT_NT, L_kv));
+    if constexpr (!DENSE) prefetch_words(P0, n_begin, g_begin, a.off[g_begin + 1] < min(n_begin + AT_NT, L_kv));
 
     // Q^T operands: lane = query, slots (hf, j) = channel 16*ks + 8*hf + j
     const int q_base = qt * QT + wave * QW + lr;
@@ -612,13 +618,13 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     // jt + 1 dequantized into the other LDS buffer. With ROPE, a tile is
     // rotated in place (one more barrier) before its compute.
     auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-    int jt = 0;
-    if constexpr (DENSE) prefetch(P0, 0);
-    dequant(0, P0, 0);
-    if (nt > 1) prefetch(P0, AT_NT);
+    int jt = t_begin;
+    if constexpr (DENSE) prefetch(P0, n_begin);
+    dequant(0, P0, n_begin);
+    if (t_begin + 1 < t_end) prefetch(P0, n_begin + AT_NT);
     lds_barrier();
-    for (; jt + 1 < nt; ++jt) {
-        const int cur = jt & 1;
+    for (; jt + 1 < t_end; ++jt) {
+        const int cur = (jt - t_begin) & 1;
         const int n0 = jt * AT_NT;
         if constexpr (ROPE) {
             rope_tile(cur, n0);
@@ -628,14 +634,38 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         // overlaps its last matrix ops
         compute(cur, n0, false);
         dequant(cur ^ 1, P0, n0 + AT_NT);
-        if (jt + 2 < nt) prefetch(P0, n0 + 2 * AT_NT);
+        if (jt + 2 < t_end) prefetch(P0, n0 + 2 * AT_NT);
         lds_barrier();
     }
     if constexpr (ROPE) {
-        rope_tile(jt & 1, jt * AT_NT);
+        rope_tile((jt - t_begin) & 1, jt * AT_NT);
         lds_barrier();
     }
-    compute(jt & 1, jt * AT_NT, true);
+    compute((jt - t_begin) & 1, jt * AT_NT, jt + 1 == nt);
+
+    // ---------------- one KV range of several: unnormalized O and (m, l)
+    if (a.kv_splits > 1) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qi = q_base + 32 * qb;
+            const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+            if (qi < a.Lq) {
+                const int64_t row = ((int64_t)split * a.B * a.H + bh) * a.Lq + qi;
+                float *po = a.part_o + row * D;
+#pragma unroll
+                for (int d = 0; d < DBLK; ++d) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int ch = 32 * d + 8 * r4 + 4 * hf;
+                        *reinterpret_cast<float4 *>(po + ch) =
+                            make_float4(o[qb][d][4 * r4], o[qb][d][4 * r4 + 1], o[qb][d][4 * r4 + 2], o[qb][d][4 * r4 + 3]);
+                    }
+                }
+                if (hf == 0) *reinterpret_cast<float2 *>(a.part_ml + 2 * row) = make_float2(m_run[qb], l_tot);
+            }
+        }
+        return;
+    }
 
     // ---------------- normalise and store
 #pragma unroll
@@ -660,6 +690,41 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     }
 }
 
+// Combine the KV ranges of a split launch: with m* the largest range maximum
+// and w_s = 2^(m_s - m*), O = sum_s w_s O_s / sum_s w_s l_s, stored as bf16.
+// One thread per 4 channels of one (batch, head, query).
+__global__ __launch_bounds__(256) void merge_kv_splits(const AttnArgs a, int D) {
+    const int64_t q4 = D / 4;
+    const int64_t n = (int64_t)a.B * a.H * a.Lq * q4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int c4 = (int)(i % q4);
+    const int64_t bhq = i / q4;                        // (b*H + h) * Lq + qi
+    const int qi = (int)(bhq % a.Lq);
+    const int bh = (int)(bhq / a.Lq);
+    const int b = bh / a.H, h = bh % a.H;
+    const int64_t stride = (int64_t)a.B * a.H * a.Lq;  // rows per split
+    float m_star = -INFINITY;
+    for (int s = 0; s < a.kv_splits; ++s) m_star = fmaxf(m_star, a.part_ml[2 * (s * stride + bhq)]);
+    float l = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < a.kv_splits; ++s) {
+        const int64_t row = s * stride + bhq;
+        const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * row);
+        const float w = __builtin_amdgcn_exp2f(ml.x - m_star);
+        const float4 v = *reinterpret_cast<const float4 *>(a.part_o + row * D + 4 * c4);
+        l = __builtin_fmaf(w, ml.y, l);
+        acc.x = __builtin_fmaf(w, v.x, acc.x); acc.y = __builtin_fmaf(w, v.y, acc.y);
+        acc.z = __builtin_fmaf(w, v.z, acc.z); acc.w = __builtin_fmaf(w, v.w, acc.w);
+    }
+    const float inv = 1.0f / l;
+    uint16_t *orow = a.out + (int64_t)b * a.so_b + (int64_t)qi * a.so_l + (int64_t)h * a.so_h + 4 * c4;
+    uint2 v;
+    v.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    v.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2 *>(orow) = v;
+}
+
 #ifndef VARQ_ATTN_QB
 #define VARQ_ATTN_QB 1
 #endif
@@ -671,7 +736,7 @@ constexpr int AT_CFG_NW = VARQ_ATTN_NW;
 
 template <int BITS, int D>
 static hipError_t launch_at(const AttnArgs &a, hipStream_t st) {
-    const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H;
+    const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H * a.kv_splits;
     const int64_t grid = (n_blocks + 7) / 8 * 8;
     if (a.rcos) {
         hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW, false, true>), dim3((unsigned)grid),
@@ -708,7 +773,7 @@ int attention_q_tile() { return 32 * AT_CFG_QB * AT_CFG_NW; }
 // Dense bf16 K/V (the unfused baseline): the same pipeline and compute, with
 // tiles staged from bf16 rows instead of dequantized from packed words.
 hipError_t launch_dense_attention(const AttnArgs &a, int D, hipStream_t st) {
-    const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H;
+    const int64_t n_blocks = (int64_t)a.n_qtiles * a.B * a.H * a.kv_splits;
     const int64_t grid = (n_blocks + 7) / 8 * 8;
     if (D == 64)
         hipLaunchKernelGGL((packed_attention_v5<16, 64, AT_CFG_QB, AT_CFG_NW, false>), dim3((unsigned)grid),
@@ -718,13 +783,21 @@ hipError_t launch_dense_attention(const AttnArgs &a, int D, hipStream_t st) {
                            dim3(64 * AT_CFG_NW), 0, st, a);
     else
         return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.kv_splits == 1) return e;
+    const int64_t n = (int64_t)a.B * a.H * a.Lq * (D / 4);
+    hipLaunchKernelGGL(merge_kv_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, D);
     return hipGetLastError();
 }
 
 hipError_t launch_packed_attention(const AttnArgs &a, int D, int bits, hipStream_t st) {
-    if (D == 64) return launch_at_bits<64>(a, bits, st);
-    if (D == 128) return launch_at_bits<128>(a, bits, st);
-    return hipErrorInvalidValue;
+    hipError_t e = hipErrorInvalidValue;
+    if (D == 64) e = launch_at_bits<64>(a, bits, st);
+    if (D == 128) e = launch_at_bits<128>(a, bits, st);
+    if (e != hipSuccess || a.kv_splits == 1) return e;
+    const int64_t n = (int64_t)a.B * a.H * a.Lq * (D / 4);
+    hipLaunchKernelGGL(merge_kv_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, D);
+    return hipGetLastError();
 }
 
 }  // namespace varq

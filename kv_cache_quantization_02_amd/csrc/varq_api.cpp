@@ -89,6 +89,8 @@ struct Scratch {
     uint32_t *sync = nullptr;
     uint64_t *slots = nullptr;
     size_t n_slots = 0;
+    float *attn = nullptr;      // attention partials of KV-split launches
+    size_t attn_bytes = 0;
 };
 std::mutex g_scratch_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
@@ -123,6 +125,90 @@ int scratch_for(hipStream_t st, size_t n_slots, uint32_t **sync, uint64_t **slot
     return VARQ_OK;
 }
 
+
+// Attention partials for a launch split over KV ranges, per (device, stream),
+// grown on demand (after synchronizing that stream) and kept until the
+// process ends. Every launch writes all the partials it reads.
+int attn_scratch_for(hipStream_t st, size_t bytes, float **p_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VARQ_ELAUNCH, "packed_attention: no current device");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    Scratch &s = g_scratch[{dev, st}];
+    if (s.attn_bytes < bytes) {
+        if (s.attn) {
+            if (hipStreamSynchronize(st) != hipSuccess || hipFree(s.attn) != hipSuccess)
+                return fail(VARQ_ELAUNCH, "packed_attention: cannot release scratch");
+            s.attn = nullptr;
+            s.attn_bytes = 0;
+        }
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess) return fail(VARQ_ELAUNCH, "packed_attention: scratch allocation failed");
+        s.attn = static_cast<float *>(p);
+        s.attn_bytes = bytes;
+    }
+    *p_out = s.attn;
+    return VARQ_OK;
+}
+
+int device_cus() {
+    static std::mutex mu;
+    static std::map<int, int> cus;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cus.find(dev);
+    if (it != cus.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev] = n;
+    return n;
+}
+
+// Number of KV ranges for an attention launch of `wgs` work-groups over `nt`
+// 64-token tiles: 1 when the grid fills at least two rounds of resident
+// work-groups; otherwise the count (ranges of at least 8 tiles) that
+// minimizes rounds x (tiles per range + 4), the 4 standing for a work-group's
+// fixed cost (query load, first tile, output).
+int plan_kv_splits(int64_t wgs, int nt, int per_cu) {
+    const int cus = device_cus();
+    if (cus <= 0) return 1;
+    const int64_t slots = (int64_t)cus * per_cu;
+    if (wgs >= 2 * slots) return 1;
+    auto cost = [&](int S) {
+        const int64_t rounds = (wgs * S + slots - 1) / slots;
+        return rounds * ((nt + S - 1) / S + 4);
+    };
+    int best = 1;
+    for (int S = 2; S <= varq::VARQ_MAX_KV_SPLITS && nt / S >= 8; ++S)
+        if (cost(S) < cost(best)) best = S;
+    return best;
+}
+
+// KV ranges of an attention launch (a.off, a.L_kv, a.Lq, a.B, a.H and
+// a.n_qtiles set): one range, or the planned split with its partials scratch.
+int setup_kv_ranges(varq::AttnArgs &a, int D, void *stream) {
+    const int nt = (int)((a.L_kv + 63) / 64);
+    a.kv_splits = 1;
+    a.split_t0[0] = 0;
+    a.split_t0[1] = nt;
+    a.split_g0[0] = 0;
+    const int S = plan_kv_splits((int64_t)a.n_qtiles * a.B * a.H, nt, D == 64 ? 2 : 1);
+    if (S == 1) return VARQ_OK;
+    a.kv_splits = S;
+    int g = 0;
+    for (int k = 0; k < S; ++k) {
+        a.split_t0[k] = (int32_t)((int64_t)nt * k / S);
+        while (a.off[g + 1] <= (int64_t)a.split_t0[k] * 64) ++g;
+        a.split_g0[k] = g;
+    }
+    a.split_t0[S] = nt;
+    const size_t rows = (size_t)S * a.B * a.H * a.Lq;
+    float *part = nullptr;
+    if (int r = attn_scratch_for(static_cast<hipStream_t>(stream), rows * (D + 2) * sizeof(float), &part)) return r;
+    a.part_o = part;
+    a.part_ml = part + rows * D;
+    return VARQ_OK;
+}
 }  // namespace
 
 namespace {
@@ -512,6 +598,8 @@ int packed_attention_impl(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
     a.rcos = rcos; a.rsin = rsin;
     for (int g = 0; g <= G; ++g) a.off[g] = group_offsets[g];
+    // an under-filled grid runs its KV tiles in ranges, merged afterwards
+    if (int r = setup_kv_ranges(a, D, stream)) return r;
     return launch_status(varq::launch_packed_attention(a, D, bits, static_cast<hipStream_t>(stream)),
                          "packed_attention");
 }
@@ -589,6 +677,7 @@ int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
     a.off[0] = 0;
     a.off[1] = (int32_t)L_kv;
+    if (int r = setup_kv_ranges(a, D, stream)) return r;
     return launch_status(varq::launch_dense_attention(a, D, static_cast<hipStream_t>(stream)), "bf16_attention");
 }
 

@@ -65,6 +65,8 @@ struct GroupArgs {
     int32_t off[VARQ_MAX_GROUPS_DEV + 1];
 };
 
+constexpr int VARQ_MAX_KV_SPLITS = 8;
+
 struct AttnArgs {
     const uint16_t *q;          // bf16 [B, Lq, H, D]
     int64_t sq_b, sq_l, sq_h;
@@ -78,6 +80,14 @@ struct AttnArgs {
     int B, H, W, G;
     int n_qtiles;
     float scale_log2;           // softmax_scale * log2(e)
+    // the KV tiles split into kv_splits ranges [split_t0[s], split_t0[s + 1])
+    // (64-token tiles), split s starting in block split_g0[s]; with more than
+    // one split every work-group writes its unnormalized O and its (m, l) to
+    // part_o [S, B*H, Lq, D] and part_ml [S, B*H, Lq, 2] (fp32) for the merge
+    int kv_splits;
+    int32_t split_t0[VARQ_MAX_KV_SPLITS + 1];
+    int32_t split_g0[VARQ_MAX_KV_SPLITS];
+    float *part_o, *part_ml;
     int32_t off[VARQ_MAX_GROUPS_DEV + 1];
 };
 

@@ -359,6 +359,34 @@ def test_attention_running_maximum_jumps(V, D, bits):
         _assert_attn(_gpu_rows(out), ob, C, tag=f"{name} D={D} bits={bits}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_attention_kv_split_small_grid(V, D, bits):
+    """Few work-groups over a long cache: the KV tiles run in several ranges
+    whose partial (O, m, l) are merged with log-sum-exp weights. Ragged queries,
+    a partial last tile, block boundaries inside tiles and inside ranges, and
+    one block far larger than the rest (range maxima differ widely)."""
+    _say(f"[attn kv split D={D} bits={bits}]")
+    g = torch.Generator().manual_seed(21 + D + bits)
+    B, H, L, Lq = 1, 2, 3000, 300
+    off = [0, 700, 1500, 2222, 3000]
+    k = torch.randn(B, L, H, D, generator=g)
+    k[:, 1500:2222] *= 30
+    k = k.to(torch.bfloat16)
+    v = (torch.randn(B, L, H, D, generator=g) * 2).to(torch.bfloat16)
+    q = torch.randn(B, Lq, H, D, generator=g).to(torch.bfloat16)
+    out, (pk, sk, pv, sv) = _gpu_attention(V, k.to(DEV), v.to(DEV), q.to(DEV), off, bits)
+    _, C, ob = _oracle_attention(k, v, q, off, bits)
+    _assert_attn(_gpu_rows(out), ob, C, tag=f"D={D} bits={bits}")
+    # the unfused path (dense bf16 attention over unpacked K, V) splits the
+    # same way and gives the same bits
+    kd = V.unpack_dequant(pk, sk, off, bits)
+    vd = V.unpack_dequant(pv, sv, off, bits)
+    unfused = V.bf16_attention(q.to(DEV), kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(unfused.view(torch.int16), out.view(torch.int16))
+
+
 def test_attention_strided_q_out(V):
     _say("[attn strided q/out]")
     g = torch.Generator().manual_seed(4)
