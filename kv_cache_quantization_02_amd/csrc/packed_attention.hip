@@ -5,24 +5,28 @@
 // README "Deployment Results" / "Memory-Efficient Runtime": loading the packed
 // cache, unpacking and dequantizing are fused into attention.
 //
-// Work-group = 4 waves x 64 queries of one (batch, head); KV tiles of 64 tokens,
-// software pipelined with one LDS barrier per tile:
-//  * packed words of tile j+2 are fetched from HBM into registers (each thread
-//    owns one (word plane, 8 consecutive tokens) item = one 32-byte load);
-//  * tile j+1 is dequantized exactly, bf16_rne(q * s[block(t), c]), from those
-//    registers into the free half of a double-buffered LDS - K row-major
-//    (token x channel), V transposed (channel x token) - placed right after the
-//    first matrix-core batch of tile j so that it overlaps it;
+// Work-group = 8 waves x 32 queries of one (batch, head) and one range of the
+// KV tiles (the whole window unless the grid is too small to fill the device;
+// then the ranges' partial results are merged by merge_kv_splits). Tiles of 64
+// tokens are software pipelined with one LDS barrier per tile:
+//  * the packed words of tile j+2 are fetched into registers (an item = 4
+//    consecutive tokens of one word plane = one 16-byte load per thread);
 //  * tile j is consumed by each wave: S^T = K Q^T with v_mfma_f32_32x32x16_bf16
-//    (lanes own one query each, so softmax statistics are lane-local), an online
-//    base-2 softmax in fp32 that rescales the accumulators only when some lane's
-//    running maximum grows by more than 2^8, and O^T += V^T P^T with P taken
-//    straight from the S^T accumulators (their layout is the B-operand layout of
-//    the PV product up to a fixed permutation of each 16-token k-step, which the
-//    V^T layout follows). Every K/V operand read from LDS feeds the wave's two
-//    32-query blocks. Row sums use v_dot2 on the bf16 P actually multiplied.
-// Only the last tile masks tokens past the window; only tiles that contain a
-// block boundary take the per-token scale path.
+//    (a lane owns one query, so softmax statistics are lane-local), base-2
+//    softmax in fp32 against a running maximum that is raised only when a
+//    half-tile's exponentials leave [0, 2^64), and O^T += V^T P^T with P taken
+//    straight from the S^T accumulators (their layout is the B-operand layout
+//    of the PV product up to a fixed permutation of each 16-token k-step, which
+//    the V^T layout follows). Row sums use v_dot2 on the bf16 P actually
+//    multiplied. The second half's score MFMAs are interleaved with the first
+//    half's exponentials, and the first half's P*V with the second half's
+//    exponentials: the matrix core and the vector ALUs overlap only when their
+//    instructions alternate within one wave;
+//  * tile j+1 is then dequantized exactly, bf16_rne(q * s[block(t), c]), from
+//    the registers into the free half of the double-buffered LDS - K row-major
+//    (token x channel), V transposed (channel x token).
+// Only the last tile of the window masks tokens past it; only tiles that
+// contain a block boundary take the per-token scale path.
 #include "varq_device.h"
 
 namespace varq {

@@ -13,7 +13,10 @@
 // quotient and writes whole words: at 2, 4, 7 and 8 bits a lane's 8 channels
 // (a lane pair's 16 at 2 bits) form whole words directly; at 3, 5 and 6 bits
 // the fields are staged in LDS and stored plane by plane. Either way the lanes
-// of a work-group cover every token of the unit in each word plane.
+// of a work-group cover every token of the unit in each word plane. When every
+// block fits one unit, a second tensor of the same shape and block map (V next
+// to K) can ride in the same launch: unit ids past the first tensor's units
+// address the second tensor's input, words and scales.
 //
 // A block split over several chunks needs the maximum over all of them. Each
 // chunk publishes its partial maxima in a scratch slot tagged with this
