@@ -432,6 +432,10 @@ def main():
     n_at_per_step = max(1, len(at_b))
     qp_avg_ms = sum(qp_ms) / len(qp_ms) if qp_ms else 0.0
     at_avg_ms = sum(at_ms) / len(at_ms) if at_ms else 0.0
+
+    def median(xs):
+        xs = sorted(xs)
+        return 0.0 if not xs else (xs[len(xs) // 2] if len(xs) % 2 else 0.5 * (xs[len(xs) // 2 - 1] + xs[len(xs) // 2]))
     qp_bytes_per_launch = sum(qp_b) / n_qp_per_step
     at_bytes_per_launch = sum(at_b) / n_at_per_step
     at_flops_per_launch = sum(at_f) / n_at_per_step
@@ -440,10 +444,12 @@ def main():
     at_tflops = at_flops_per_launch / (at_avg_ms * 1e-3) / 1e12 if at_avg_ms else 0.0
 
     kernels = {
-        "quant_pack": {"avg_ms": round(qp_avg_ms, 5), "launches_per_step": len(qp_b),
+        "quant_pack": {"avg_ms": round(qp_avg_ms, 5), "median_ms": round(median(qp_ms), 5),
+                       "launches_per_step": len(qp_b),
                        "alg_bytes_per_launch": int(qp_bytes_per_launch), "GB/s": round(qp_gbs, 1),
                        "hbm_frac": round(qp_gbs / HBM_PEAK_GBS, 4)},
-        "packed_attention": {"avg_ms": round(at_avg_ms, 5), "launches_per_step": len(at_b),
+        "packed_attention": {"avg_ms": round(at_avg_ms, 5), "median_ms": round(median(at_ms), 5),
+                             "launches_per_step": len(at_b),
                              "alg_bytes_per_launch": int(at_bytes_per_launch),
                              "alg_flops_per_launch": at_flops_per_launch,
                              "GB/s": round(at_gbs, 1), "hbm_frac": round(at_gbs / HBM_PEAK_GBS, 4),
