@@ -118,9 +118,10 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
  * same result as varq_quantize_pack(k -> packed_k, scales_k) followed by
  * varq_quantize_pack(v -> packed_v, scales_v), with one shape, block map and
  * cache layout for both. k and v have strides of their own; packed_k/packed_v
- * and scales_k/scales_v are distinct buffers. When every block fits one
- * work-group's 16384 elements both tensors go through one launch; otherwise
- * the cooperative kernel runs once per tensor (same scratch rules as above).
+ * and scales_k/scales_v are distinct buffers. Both tensors go through one
+ * launch (the cooperative kernel when some block is longer than one
+ * work-group's 16384 elements, with the scratch rules above counting the
+ * chunks and blocks of both tensors).
  * Errors: those of varq_quantize_pack, for either tensor, and VARQ_EINVAL when
  * K and V share a cache buffer.
  */

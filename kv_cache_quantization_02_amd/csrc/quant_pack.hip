@@ -58,7 +58,7 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Wave-uniform description of a unit.
 struct Unit {
-    int64_t id, bh;      // id within its tensor
+    int64_t id, bh;      // id over the launch (both tensors), (batch*H + head)
     int t;               // tensor: 0 = x, 1 = x2 (one launch for K and V)
     int g0, nb;          // first block, number of blocks (> 1 only for packs)
     int c, nc;           // chunk index and chunk count of block g0 (nc == 1 for packs)
@@ -84,9 +84,9 @@ __device__ inline int lds_uniform(const int32_t *p) { return __builtin_amdgcn_re
 
 __device__ inline Unit unit_of(const QuantPackArgs &a, const Tables &tb, int64_t id) {
     Unit U;
+    U.id = id;
     U.t = id >= a.n_units_one;
     if (U.t) id -= a.n_units_one;
-    U.id = id;
     U.bh = id / a.units_per_bh;
     const int r_in = (int)(id - U.bh * a.units_per_bh);
     int lo = 0, hi = a.G;                 // last g with unit_start[g] <= r_in
@@ -541,6 +541,11 @@ __device__ inline float put_scale(float *sh_s, float *sh_y, int slot, int D, int
     return s;
 }
 
+// Row of the block maxima exchanged for block g0 of unit U: [tensor][b*H + h][block].
+__device__ inline int64_t fin_row(const QuantPackArgs &a, const Unit &U) {
+    return ((int64_t)U.t * a.B * a.H + U.bh) * a.G + U.g0;
+}
+
 __device__ inline float *scale_ptr(const QuantPackArgs &a, const Unit &U, int tid) {
     return (U.t ? a.scales2 : a.scales) + (U.bh * a.G_cap + a.group_start + U.g0) * a.D + tid;
 }
@@ -639,7 +644,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
         const bool last1 = has1 && U1.c == U1.nc - 1;
 
         // block maximum for D2, published by its block's last chunk
-        const uint64_t *fin2 = a.fin + (U2.bh * a.G + U2.g0) * D + tid;
+        const uint64_t *fin2 = a.fin + fin_row(a, U2) * D + tid;
         uint64_t v2 = 0;
         if (has2 && tid < D) v2 = load_slot(fin2);
 
@@ -668,7 +673,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
             }
             if (last1) {
                 const float m = gather_partials(a.part + (U1.id - U1.c) * D + tid, U1.nc, D, 0.0f, epoch, status);
-                __hip_atomic_store(a.fin + (U1.bh * a.G + U1.g0) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
+                __hip_atomic_store(a.fin + fin_row(a, U1) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
                 *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, D, tid, m);
             }
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
     if (has1 && U1.c == U1.nc - 1) {
         if (tid < D) {
             const float m = gather_partials(a.part + (U1.id - U1.c) * D + tid, U1.nc, D, 0.0f, epoch, status);
-            __hip_atomic_store(a.fin + (U1.bh * a.G + U1.g0) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
+            __hip_atomic_store(a.fin + fin_row(a, U1) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, D, tid, m);
         }
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
     }
     if (has2) {
         if (tid < D) {
-            const uint64_t *fin2 = a.fin + (U2.bh * a.G + U2.g0) * D + tid;
+            const uint64_t *fin2 = a.fin + fin_row(a, U2) * D + tid;
             put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin2, load_slot(fin2), epoch, status));
         }
         lds_barrier();
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
     }
     if (has1) {
         if (tid < D) {
-            const uint64_t *fin1 = a.fin + (U1.bh * a.G + U1.g0) * D + tid;
+            const uint64_t *fin1 = a.fin + fin_row(a, U1) * D + tid;
             put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin1, load_slot(fin1), epoch, status));
         }
         lds_barrier();

@@ -329,7 +329,7 @@ int qp_launch(varq::QuantPackArgs &a, int bits, bool split, int max_nc, void *st
         if (max_nc > grid)
             return fail(VARQ_EUNSUPPORTED, "quantize_pack: a block of %d chunks exceeds the %d resident work-groups",
                         max_nc, grid);
-        const size_t bhg = (size_t)a.B * a.H * a.G;
+        const size_t bhg = (size_t)(a.x2 ? 2 : 1) * a.B * a.H * a.G;
         uint32_t *sync = nullptr;
         uint64_t *slots = nullptr;
         if (int r = scratch_for(static_cast<hipStream_t>(stream), ((size_t)a.n_units + bhg) * D, &sync, &slots))
@@ -404,11 +404,6 @@ int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_
     if (empty) return ok();
     if (packed_k == packed_v || scales_k == scales_v)
         return fail(VARQ_EINVAL, "quantize_pack_kv: K and V need caches of their own");
-    if (split) {
-        // blocks longer than one unit: the cooperative kernel, once per tensor
-        if (int r = qp_launch(a, bits, split, max_nc, stream)) return r;
-        return qp_launch(av, bits, split, max_nc, stream);
-    }
     a.x2 = av.x;
     a.sx2_b = av.sx_b; a.sx2_l = av.sx_l; a.sx2_h = av.sx_h;
     a.packed2 = av.packed;

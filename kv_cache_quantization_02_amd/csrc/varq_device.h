@@ -33,8 +33,8 @@ struct QuantPackArgs {
     uint32_t *packed2;
     float *scales2;
     int64_t n_units_one;        // units of one tensor (n_units when x2 is null)
-    uint64_t *part;             // [n_units, D]
-    uint64_t *fin;              // [B*H*G, D]
+    uint64_t *part;             // [n_units, D] (both tensors)
+    uint64_t *fin;              // [T*B*H*G, D], T = 2 with x2
     uint32_t *sync;             // [3]
     int64_t L_cap, tok_start, G_cap, group_start;
     int64_t n_units;
