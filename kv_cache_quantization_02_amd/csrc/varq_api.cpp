@@ -209,9 +209,6 @@ int setup_kv_ranges(varq::AttnArgs &a, int D, void *stream) {
     a.part_ml = part + rows * D;
     return VARQ_OK;
 }
-}  // namespace
-
-namespace {
 
 // Validates one tensor's quantize+pack arguments and fills the launch
 // arguments; *empty is set when there is nothing to write.
