@@ -387,6 +387,47 @@ def test_attention_kv_split_small_grid(V, D, bits):
     assert torch.equal(unfused.view(torch.int16), out.view(torch.int16))
 
 
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_attention_head_dim_64_many_blocks(V, bits):
+    """head_dim 64 with more blocks than a work-group keeps in LDS (40 > 32):
+    scales stream with the words; blocks of 1 to 80 tokens, so tiles hold
+    several boundaries, and a window that ends inside a tile."""
+    _say(f"[attn d64 many blocks bits={bits}]")
+    g = torch.Generator().manual_seed(31 + bits)
+    sizes = [1, 3, 7, 2, 80, 5, 9, 33, 64, 1] * 4
+    off = [0]
+    for n in sizes:
+        off.append(off[-1] + n)
+    B, H, D, L, Lq = 2, 3, 64, off[-1], 90
+    k = (torch.randn(B, L, H, D, generator=g) * 3).to(torch.bfloat16)
+    v = (torch.randn(B, L, H, D, generator=g) * 2).to(torch.bfloat16)
+    q = torch.randn(B, Lq, H, D, generator=g).to(torch.bfloat16)
+    out, _ = _gpu_attention(V, k.to(DEV), v.to(DEV), q.to(DEV), off, bits)
+    _, C, ob = _oracle_attention(k, v, q, off, bits)
+    _assert_attn(_gpu_rows(out), ob, C, tag=f"G={len(off) - 1} L={L}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bits", [5, 6, 7])
+def test_attention_odd_bit_widths(V, D, bits):
+    """INT5/6/7 caches (6, 5 and 4 codes per word; at INT6 the last word of a
+    row is partly empty) with ragged blocks and queries."""
+    _say(f"[attn bits={bits} D={D}]")
+    g = torch.Generator().manual_seed(41 + bits + D)
+    B, H, L, Lq = 2, 3, 300, 70
+    off = [0, 1, 5, 64, 150, 151, 300]
+    for unit_v in (False, True):
+        k = (torch.randn(B, L, H, D, generator=g) * 3).to(torch.bfloat16)
+        v = torch.randn(B, L, H, D, generator=g)
+        if not unit_v:
+            v[..., :6] *= 30                                  # outlier channels
+        v = v.to(torch.bfloat16)
+        q = torch.randn(B, Lq, H, D, generator=g).to(torch.bfloat16)
+        out, _ = _gpu_attention(V, k.to(DEV), v.to(DEV), q.to(DEV), off, bits)
+        _, C, ob = _oracle_attention(k, v, q, off, bits)
+        _assert_attn(_gpu_rows(out), ob, C, literal=unit_v, tag=f"unit_v={unit_v}")
+
+
 def test_attention_strided_q_out(V):
     _say("[attn strided q/out]")
     g = torch.Generator().manual_seed(4)
