@@ -91,6 +91,8 @@ def test_kv_split_blocks(V):
     k = (torch.randn(B, L, H, D, generator=g) * 2).to(torch.bfloat16)
     v = torch.randn(B, L, H, D, generator=g).to(torch.bfloat16)
     _check(V, k, v, [0, 4, 300, 700], 4)
+    # the same blocks appended at an offset of a larger cache
+    _check(V, k, v, [0, 4, 300, 700], 3, tok_start=40, group_start=2, extra_rows=24, extra_groups=1)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
