@@ -123,3 +123,29 @@ def test_kv_equals_two_calls_on_a_long_cache(V):
     for a, b in ((pk, qk), (pv, qv), (sk.view(torch.int32), tk.view(torch.int32)),
                  (sv.view(torch.int32), tv.view(torch.int32))):
         assert torch.equal(a, b)
+
+
+def test_kv_split_repeated_calls_alternating_shapes(V):
+    """The cooperative launch over both tensors, called repeatedly on one stream
+    with alternating shapes (its exchange scratch is reused and re-tagged every
+    launch): every call writes exactly what two single-tensor calls write."""
+    _say("[kv split repeat]")
+    g = torch.Generator(device=DEV).manual_seed(9)
+    cases = []
+    for (B, L, H, D, off) in ((1, 700, 3, 128, [0, 4, 300, 700]), (2, 2000, 2, 64, [0, 900, 2000]),
+                              (1, 1560, 4, 128, [0, 1560])):
+        k = (torch.randn(B, L, H, D, generator=g, device=DEV) * 3).to(torch.bfloat16)
+        v = torch.randn(B, L, H, D, generator=g, device=DEV).to(torch.bfloat16)
+        ref = _caches(V, B, H, D, L, len(off) - 1, 4)
+        V.quantize_pack(k, off, 4, ref[0], ref[1])
+        V.quantize_pack(v, off, 4, ref[2], ref[3])
+        cases.append((k, v, off, ref))
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for (k, v, off, ref) in cases:
+            B, L, H, D = k.shape
+            got = _caches(V, B, H, D, L, len(off) - 1, 4)
+            V.quantize_pack_kv(k, v, off, 4, *got)
+            torch.cuda.synchronize()
+            for a, b in zip(got, ref):
+                assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, k.shape)
