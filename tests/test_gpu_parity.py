@@ -428,6 +428,26 @@ def test_attention_odd_bit_widths(V, D, bits):
         _assert_attn(_gpu_rows(out), ob, C, literal=unit_v, tag=f"unit_v={unit_v}")
 
 
+def test_attention_kv_split_scratch_reuse(V):
+    """Split launches of different shapes alternate on one stream (the partials
+    scratch is reused and grown): every call repeats its first result bit for bit."""
+    _say("[attn kv split scratch reuse]")
+    g = torch.Generator(device=DEV).manual_seed(13)
+    cases = []
+    for (B, H, D, L, Lq, off) in ((1, 2, 64, 1500, 100, [0, 700, 1500]), (1, 3, 128, 4000, 300, [0, 1000, 4000]),
+                                  (2, 1, 128, 2500, 64, [0, 2500])):
+        k = (torch.randn(B, L, H, D, generator=g, device=DEV) * 2).to(torch.bfloat16)
+        v = torch.randn(B, L, H, D, generator=g, device=DEV).to(torch.bfloat16)
+        q = torch.randn(B, Lq, H, D, generator=g, device=DEV).to(torch.bfloat16)
+        out, cache = _gpu_attention(V, k, v, q, off, 4)
+        cases.append((q, off, cache, out.clone()))
+    for rep in range(3):
+        for (q, off, (pk, sk, pv, sv), first) in reversed(cases) if rep % 2 else cases:
+            out = V.packed_attention(q, pk, sk, pv, sv, off, 4)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), first.view(torch.int16)), (rep, q.shape)
+
+
 def test_attention_strided_q_out(V):
     _say("[attn strided q/out]")
     g = torch.Generator().manual_seed(4)
