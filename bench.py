@@ -207,7 +207,8 @@ def unfused_compare(varq, torch, wl, bits, launches, off, q, pk, sk, pv, sv, arg
     ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
     return {"path": "unpack_dequant(K), unpack_dequant(V) into bf16, then bf16_attention",
             "avg_ms_per_call": round(ms, 5), "fused_avg_ms_per_call": round(fused_ms, 5),
-            "fused_speedup": round(ms / fused_ms, 3) if fused_ms else None}
+            "fused_speedup": round(ms / fused_ms, 3) if fused_ms else None,
+            "dequant_workspace_bytes": int(kd.numel() * kd.element_size() * 2)}
 
 
 # ---------------------------------------------------------------- grouping report
@@ -470,7 +471,19 @@ def main():
                 "frac": round(at_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": (tr["fetch_bytes"] + tr["write_bytes"]) if tr else None}
 
+    fused_peak = torch.cuda.max_memory_allocated()
     unfused = unfused_compare(varq, torch, wl, bits, launches, off, q, pk, sk, pv, sv, args, at_avg_ms)
+    # persistent cache sizes (exact preallocation) against the bf16 cache, and
+    # the dequant workspace the unfused path needs (the fused path needs none)
+    pb, sb = varq.cache_bytes(B, H, D, pk.shape[3], G, bits)
+    bf16_bytes = B * L * H * D * 2
+    memory = {"packed_bytes_per_tensor": int(pb), "scale_bytes_per_tensor": int(sb),
+              "bf16_bytes_per_tensor": int(bf16_bytes),
+              "cache_fraction_of_bf16": round((pb + sb) / bf16_bytes, 5),
+              "fused_dequant_workspace_bytes": 0,
+              "unfused_dequant_workspace_bytes": unfused["dequant_workspace_bytes"] if unfused else None,
+              "device_peak_bytes_fused_step": int(fused_peak),
+              "device_peak_bytes_with_unfused": int(torch.cuda.max_memory_allocated())}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -499,6 +512,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "unfused": unfused,
+        "memory": memory,
     }
     print(json.dumps(line), flush=True)
 
