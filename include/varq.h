@@ -14,7 +14,10 @@
  * Conventions for every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
  *    frees them and keeps no reference after the call returns. The only memory
- *    the library allocates is varq_quantize_pack's scratch (described there).
+ *    the library allocates is scratch it owns per (device, stream): the
+ *    cross-work-group exchange of quantize+pack for blocks longer than one
+ *    work-group, and the partial results of attention launches split over KV
+ *    ranges (both described at their entry points).
  *  - `group_offsets` is a HOST array of G+1 int32 prefix offsets
  *    0 = o_0 < o_1 < ... < o_G: block g covers tokens [o_g, o_{g+1}).
  *    G <= VARQ_MAX_GROUPS per call.
