@@ -618,7 +618,13 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
     }
 
     uint32_t *status = a.sync + 2;
-    uint32_t epoch = __hip_atomic_load(a.sync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // Relaxed atomics suffice for the epoch word: the previous launch's write
+    // is ordered before this launch by the stream, and every work-group reads
+    // the word before its own increment below, so the work-group making the
+    // last increment finds every read of this launch done. (Acquire and
+    // acq_rel orderings here would cost a whole-L2 invalidate and write-back
+    // per work-group.)
+    uint32_t epoch = __hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     if (epoch == 0) epoch = 1;
     lds_barrier();
 
@@ -723,7 +729,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
 
     // ---- the last work-group to finish advances the epoch for the next launch
     if (tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(a.sync + 1, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t done = __hip_atomic_fetch_add(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
             __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.sync, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
