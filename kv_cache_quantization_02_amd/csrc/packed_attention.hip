@@ -243,6 +243,9 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
 
     // Q^T operands: lane = query, slots (hf, j) = channel 16*ks + 8*hf + j
     const int q_base = qt * QT + wave * QW + lr;
+    // a wave whose queries all lie past Lq (the last query tile of a block
+    // that is not a multiple of the tile) only helps dequantize tiles into LDS
+    const bool wave_idle = __builtin_amdgcn_readfirstlane(qt * QT + wave * QW) >= a.Lq;
     bf16x8 qop[QB][KSTEPS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -449,6 +452,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     // with the exponentials of half 0; P*V of half 0 interleaved with the
     // exponentials of half 1; P*V of half 1.
     auto compute = [&](int buf, int n0, bool masked) {
+        if (wave_idle) return;
         const uint16_t *Kb = Ks + buf * KBUF + lr * KP + 8 * hf;
         const uint16_t *Vb = Vt + buf * VBUF + lr * VP + 8 * hf;
         floatx16 s[2][QB];
