@@ -10,9 +10,9 @@
 // once (16-byte loads, lanes along a row) and takes the per-(block, channel)
 // absmax: packed 16-bit maxima of |x| bit patterns in registers, then LDS
 // max-atomics. It quantizes from registers with the division-free exact
-// quotient and writes whole words: at 2, 4, 7 and 8 bits a lane's 8 channels
-// (a lane pair's 16 at 2 bits) form whole words directly; at 3, 5 and 6 bits
-// the fields are staged in LDS and stored plane by plane. Either way the lanes
+// quotient and writes whole words: at 4, 7 and 8 bits a lane's 8 channels
+// form whole words directly; at 2, 3, 5 and 6 bits the fields are staged in
+// LDS as code bytes and assembled into words. Either way the lanes
 // of a work-group cover every token of the unit in each word plane. When every
 // block fits one unit, a second tensor of the same shape and block map (V next
 // to K) can ride in the same launch: unit ids past the first tensor's units
@@ -20,26 +20,31 @@
 //
 // A block split over several chunks needs the maximum over all of them. Each
 // chunk publishes its partial maxima in a scratch slot tagged with this
-// launch's epoch and is deferred: the work-group keeps its rows in registers
-// and goes on with its next unit. One unit later, the block's last chunk
-// gathers the partials (waiting on each tag), publishes the block maximum the
-// same way and is quantized; two units later every other chunk reads that
-// maximum and is quantized. Each value crosses work-groups in one 64-bit
-// atomic word carrying both the tag and the maximum, so no cache flush or
-// fence is needed for it; the epoch advances once per launch, set by the last
-// work-group to finish.
+// launch's epoch. The work-group holding the block's last chunk then gathers
+// the partials with all its threads (waiting on each tag, merging in LDS),
+// publishes the block maximum the same way and quantizes its rows; the
+// work-group of every other chunk waits for that maximum and quantizes its
+// rows. A work-group holds only its current unit, as for whole blocks. Each
+// value crosses work-groups in one 64-bit atomic word carrying both the tag
+// and the maximum, so no cache flush or fence is needed for it; the epoch
+// advances once per launch, set by the last work-group to finish.
 //
 // Progress (such launches are cooperative: every work-group is resident, and
 // no block has more chunks than there are work-groups, G). Work-group w takes
-// units w, w + G, ...; in the iteration of unit x it publishes x's partial
-// P(x) before anything that can wait, then gathers for the last chunk of
-// x - G and waits for the maximum of x - 2G. Let x be the smallest unit whose
-// P never happens. The gather for x - G needs P of chunks of its block, all
-// < x. The maximum for x - 2G is published in the iteration of r + G, r its
-// block's last chunk, r + G < x; that iteration's own gather needs P of units
-// < x, and the iterations before it in that work-group end by induction. So
-// P(x) happens, a contradiction; every gather and wait then ends. Spins are
-// nevertheless bounded and report a timeout through a status word.
+// units w, w + G, ... (round k = units kG .. kG + G - 1); a block's chunks are
+// consecutive units, so it lies in one round or two adjacent ones. Every unit
+// publishes its partial before it waits for anything. A last chunk waits only
+// for partials of lower units; another chunk waits for the maximum of its
+// block's last chunk, which can lie in the next round only for the one block
+// that crosses into it. Suppose every work-group ends rounds < k. Then all
+// start round k and publish; gathers in round k end; so do the chunks of
+// blocks whose last chunk lies in round k or earlier. Let block A cross into
+// round k + 1, r its last chunk. The unit that r's work-group (and that of
+// every other chunk of A in round k + 1) takes in round k lies below A's
+// first chunk, since A has at most G chunks, in a block ending by round k:
+// those work-groups end round k, publish their chunks of A, r's gather ends
+// and A's chunks in round k end too. So every work-group ends round k. Spins
+// are nevertheless bounded and report a timeout through a status word.
 #include <mutex>
 
 #include "varq_device.h"
@@ -151,15 +156,10 @@ __device__ inline RowBlocks row_blocks(const Bounds &B, int r0) {
 }
 
 // Work-group barrier that orders LDS only. __syncthreads() also waits for
-// every outstanding global load (vmcnt), which would drain the next unit's
-// prefetch at each barrier; no wave here reads global memory another wave of
-// its work-group wrote, so LDS ordering is all that is needed.
+// every outstanding global memory operation (vmcnt), e.g. the previous
+// unit's word stores at each barrier; no wave here reads global memory another
+// wave of its work-group wrote, so LDS ordering is all that is needed.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Wait for every outstanding global load (vmcnt(0)) before a unit's stores:
-// the next unit's prefetch has then landed, so the following loop iteration
-// does not also wait for these stores to be acknowledged.
-__device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Thread (chunk, rr) holds channels [8 chunk, 8 chunk + 8) of the unit's rows
 // [8 rr, 8 rr + 8): consecutive rows, so a thread's rows rarely span two
@@ -358,14 +358,6 @@ __device__ inline void stage_words(const QuantPackArgs &a, const Unit &U, const 
                 sh_w[(2 * L.chunk) * wp + r] = w0;
                 sh_w[(2 * L.chunk + 1) * wp + r] = w1;
             }
-        } else if constexpr (BITS == 2) {
-            uint32_t half = 0;      // this lane's 16 bits in the upper half
-#pragma unroll
-            for (int j = 0; j < 8; ++j) half = __builtin_amdgcn_alignbit(f[j], half, 2);
-            // chunk ^ 1 of the same row: lane tid ^ 1 (rows hold an even number of lanes)
-            const uint32_t other = (uint32_t)__shfl_xor((int)half, 1);
-            // low half from this lane's upper half, high half from the partner's
-            if (live && (L.chunk & 1) == 0) sh_w[(L.chunk >> 1) * wp + r] = (half >> 16) | (other & 0xFFFF0000u);
         }
     }
 }
@@ -429,22 +421,18 @@ __device__ inline void store_words(const QuantPackArgs &a, const Unit &U, const 
 
 // Quantize and store unit U (rows in v) with the scales of LDS slot `slot`
 // (packs: slot = local block). pack_fast: every scale of the unit is known to
-// allow the division-free quotient. WHOLE (the whole-block kernel): no load
-// is in flight, so the stores need not wait for any (otherwise they wait for
-// the prefetch first, and the next unit then waits for no store). Ends with a
-// barrier, after which LDS may be rewritten.
-template <int BITS, bool WHOLE = false>
+// allow the division-free quotient. Ends with a barrier, after which LDS may
+// be rewritten.
+template <int BITS>
 __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, const Bounds &B, const uint4 (&v)[QP_ITEMS],
                                      const Lane &L, int slot, const float *sh_s, const float *sh_y,
                                      uint8_t *sh_codes, bool pack_fast = false) {
-    constexpr bool drain = !WHOLE;
     constexpr int CPW = 32 / BITS;
     const int tid = threadIdx.x;
     const int D = a.D;
-    // a 2-bit word takes a lane pair (16 channels); with an odd lane count per
-    // row the last chunk has no partner, so that case is staged in LDS like
-    // 3, 5 and 6 bits
-    const bool direct = (BITS == 4 || BITS == 7 || BITS == 8) || (BITS == 2 && (L.lpr & 1) == 0);
+    // a lane's 8 fields form whole words only at 4, 7 and 8 bits (a 2-bit word
+    // would need a lane pair, whose shuffle costs more registers than staging)
+    constexpr bool direct = (BITS == 4 || BITS == 7 || BITS == 8);
 
     // wave-uniform choice of the common path: one block, every scale of the
     // wave's channels allows the division-free quotient
@@ -456,7 +444,7 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
 
     const int tshift = a.rows_log2;
     const int span = 1 << tshift;
-    if (direct) {
+    if constexpr (direct) {
         // words -> LDS planes -> global, consecutive lanes on consecutive
         // tokens of a plane. Odd plane pitch T + 1: the lanes of a wave (chunks
         // x rows 8 apart) then write distinct banks.
@@ -466,7 +454,6 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
         else if (U.nb > 1 && pack_fast) stage_words<BITS, QM_PACK>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
         else stage_words<BITS, QM_GENERIC>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_w, wp);
         lds_barrier();
-        if (drain) wait_loads();
         store_words(a, U, sh_w, wp, tshift);
         lds_barrier();
         return;
@@ -477,7 +464,6 @@ __device__ inline void quantize_unit(const QuantPackArgs &a, const Unit &U, cons
     if (simple) stage_codes<BITS, true>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_codes, pitch);
     else stage_codes<BITS, false>(a, U, B, v, L, slot, sh_s, sh_y, s8, y8, cur, fast, sh_codes, pitch);
     lds_barrier();
-    if (drain) wait_loads();
     for (int i = tid; i < a.W * span; i += QP_THREADS) {
         const int w = i >> tshift, r = i & (span - 1);
         if (r >= U.n) continue;
@@ -516,19 +502,35 @@ __device__ inline float slot_max(const uint64_t *p, uint64_t v, uint32_t epoch, 
     return u2f((uint32_t)v);
 }
 
-// Maximum of m and the partial maxima of chunks 0 .. n-1 starting at slot p
-// (stride D), eight loads in flight at a time.
-__device__ inline float gather_partials(const uint64_t *p, int n, int D, float m, uint32_t epoch, uint32_t *status) {
-    for (int c0 = 0; c0 < n; c0 += 8) {
-        uint64_t v[8];
+constexpr int QP_GATHER = 16;                                 // partial-maximum loads in flight per thread
+
+// Per-channel maximum of the partial maxima of a block's n chunks, whose
+// slots are the n * D consecutive words at p (chunk-major), by the whole
+// work-group: thread t takes words t, t + QP_THREADS, ... with QP_GATHER loads
+// in flight, and merges each into gx[channel] with an LDS max-atomic (the
+// maxima are non-negative, so their bit patterns order like the values). gx
+// must hold zeros, ordered before this call by a barrier; the caller orders
+// the atomics before reading gx with another.
+__device__ inline void gather_block_max(const uint64_t *p, int n, int D, uint32_t *gx, uint32_t epoch,
+                                        uint32_t *status) {
+    const int total = n * D;
+    const int step = QP_THREADS % D;           // channel advance from word i to word i + QP_THREADS
+    int ch = threadIdx.x % D;                  // channel of the next word merged
+    for (int i0 = threadIdx.x; i0 < total; i0 += QP_GATHER * QP_THREADS) {
+        uint64_t v[QP_GATHER];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (c0 + j < n) v[j] = load_slot(p + (int64_t)(c0 + j) * D);
+        for (int j = 0; j < QP_GATHER; ++j) {
+            const int i = i0 + j * QP_THREADS;
+            if (i < total) v[j] = load_slot(p + i);
+        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (c0 + j < n) m = fmaxf(m, slot_max(p + (int64_t)(c0 + j) * D, v[j], epoch, status));
+        for (int j = 0; j < QP_GATHER; ++j) {
+            const int i = i0 + j * QP_THREADS;
+            if (i < total) atomicMax(gx + ch, f2u(slot_max(p + i, v[j], epoch, status)));
+            ch += step;
+            if (ch >= D) ch -= D;
+        }
     }
-    return m;
 }
 
 // Scale and reciprocal of maximum m into LDS slot `slot` (thread = channel).
@@ -550,18 +552,26 @@ __device__ inline float *scale_ptr(const QuantPackArgs &a, const Unit &U, int ti
     return (U.t ? a.scales2 : a.scales) + (U.bh * a.G_cap + a.group_start + U.g0) * a.D + tid;
 }
 
-template <int N>
-__device__ inline void copy_regs(uint4 (&dst)[N], const uint4 (&src)[N]) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) dst[k] = src[k];
+// Channel tid of the block maximum merged in gx for last chunk U: published
+// for the block's other chunks, stored as the block's scale and put in LDS
+// slot R (whose scale row is gx itself; each thread reads its word first).
+template <int BITS>
+__device__ inline void publish_block_max(const QuantPackArgs &a, const Unit &U, float *sh_s, float *sh_y,
+                                         const uint32_t *gx, uint32_t epoch) {
+    const int tid = threadIdx.x;
+    const float m = u2f(gx[tid]);
+    __hip_atomic_store(a.fin + fin_row(a, U) * a.D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    *scale_ptr(a, U, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, a.D, tid, m);
 }
 
 // SPLIT: some block of this launch spans several units (exchange through
 // scratch, cooperative launch). Otherwise every unit holds whole blocks and a
 // work-group just quantizes its units one after another. LDS is sized by the
-// host for this launch (regions at byte offsets a.lds_*).
+// host for this launch (regions at byte offsets a.lds_*). At most 128 VGPRs
+// (four waves per SIMD), so that four work-groups share a CU.
 template <int BITS, bool SPLIT>
-__global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackArgs a) {
+__global__ __launch_bounds__(QP_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void quant_pack_kernel(const QuantPackArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t qp_lds[];
     uint32_t *sh_max = reinterpret_cast<uint32_t *>(qp_lds + a.lds_max);   // [QP_MAX_PACK][D]
     float *sh_s = reinterpret_cast<float *>(qp_lds + a.lds_s);             // [QP_MAX_PACK + 2][D]
@@ -612,7 +622,7 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
                 if (!fast_scale_ok(sc)) sh_slow = 1;
             }
             lds_barrier();
-            quantize_unit<BITS, true>(a, U, B, X, L, 0, sh_s, sh_y, sh_codes, sh_slow == 0);
+            quantize_unit<BITS>(a, U, B, X, L, 0, sh_s, sh_y, sh_codes, sh_slow == 0);
         }
         return;
     }
@@ -628,47 +638,33 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
     if (epoch == 0) epoch = 1;
     lds_barrier();
 
-    // Per unit X: absmax; a chunk of a split block publishes its partial and
-    // is deferred. One unit later a last chunk gathers its block's partials,
-    // publishes the block maximum and is quantized; two units later any other
-    // chunk reads that maximum and is quantized. Units of whole blocks are
-    // quantized at once. The next unit's loads are issued after the exchange's
-    // loads (loads complete in issue order) and stay in flight while the
-    // ready units are quantized.
-    uint4 X[QP_ITEMS], Z[QP_ITEMS], D1[QP_ITEMS], D2[QP_ITEMS];
-    Bounds BX1;                               // deferred units are single blocks: no bounds
-#pragma unroll
-    for (int j = 0; j < QP_MAX_PACK - 1; ++j) BX1.b[j] = 0x7FFFFFFF;
-    Unit UX, UZ, U1 = {}, U2 = {};
-    bool has1 = false, has2 = false;          // D1: deferred one unit ago; D2: two units ago
-    int64_t u = blockIdx.x;
-    if (u < a.n_units) { UZ = unit_of(a, L.tb, u); load_unit(a, UZ, Z, L); }
-    while (u < a.n_units) {
-        UX = UZ;
-        copy_regs(X, Z);
-        u += step;
-        const bool last1 = has1 && U1.c == U1.nc - 1;
-
-        // block maximum for D2, published by its block's last chunk
-        const uint64_t *fin2 = a.fin + fin_row(a, U2) * D + tid;
-        uint64_t v2 = 0;
-        if (has2 && tid < D) v2 = load_slot(fin2);
-
-        const Bounds BX = bounds_of(L.tb, UX);
-        unit_absmax(a, UX, BX, X, L, sh_max);
+    // Per unit: absmax; a chunk of a split block publishes its partial. The
+    // block's last chunk gathers every partial, publishes the block maximum
+    // and is quantized; any other chunk waits for that maximum and is
+    // quantized. Units of whole blocks are quantized at once. Only the
+    // current unit is held in registers.
+    uint32_t *gx = reinterpret_cast<uint32_t *>(sh_y + QP_SLOT_R * D);   // gather row (slot R)
+    for (int64_t u = blockIdx.x; u < a.n_units; u += step) {
+        const Unit U = unit_of(a, L.tb, u);
+        uint4 X[QP_ITEMS];
+        load_unit(a, U, X, L);
+        const Bounds B = bounds_of(L.tb, U);
+        const bool split = U.nc > 1, last = split && U.c == U.nc - 1;
+        // slot R's rows were last read before the previous unit's final barrier
+        if (last && tid < D) gx[tid] = 0;
+        unit_absmax(a, U, B, X, L, sh_max);
         lds_barrier();
-        const bool splitX = UX.nc > 1;
         if (tid < D) {
             const float m0 = u2f(sh_max[tid]);
             sh_max[tid] = 0;
-            if (splitX) {
-                __hip_atomic_store(a.part + UX.id * D + tid, tagged(epoch, m0), __ATOMIC_RELAXED,
+            if (split) {
+                __hip_atomic_store(a.part + U.id * D + tid, tagged(epoch, m0), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             } else {
                 // whole blocks: scales now; block maxima in LDS are cleared
                 // for the next unit (ordered before its atomics by the barrier)
-                float *scl = scale_ptr(a, UX, tid);
-                for (int lb = 0; lb < UX.nb; ++lb) {
+                float *scl = scale_ptr(a, U, tid);
+                for (int lb = 0; lb < U.nb; ++lb) {
                     float m = m0;
                     if (lb > 0) {
                         m = u2f(sh_max[lb * D + tid]);
@@ -677,54 +673,22 @@ __global__ __launch_bounds__(QP_THREADS) void quant_pack_kernel(const QuantPackA
                     scl[(int64_t)lb * D] = put_scale<BITS>(sh_s, sh_y, lb, D, tid, m);
                 }
             }
-            if (last1) {
-                const float m = gather_partials(a.part + (U1.id - U1.c) * D + tid, U1.nc, D, 0.0f, epoch, status);
-                __hip_atomic_store(a.fin + fin_row(a, U1) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, D, tid, m);
+        }
+        int slot = 0;
+        if (last) {
+            gather_block_max(a.part + (U.id - U.c) * D, U.nc, D, gx, epoch, status);
+            lds_barrier();
+            if (tid < D) publish_block_max<BITS>(a, U, sh_s, sh_y, gx, epoch);
+            slot = QP_SLOT_R;
+        } else if (split) {
+            if (tid < D) {
+                const uint64_t *fin = a.fin + fin_row(a, U) * D + tid;
+                put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin, load_slot(fin), epoch, status));
             }
-            if (has2) put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin2, v2, epoch, status));
-        }
-        if (u < a.n_units) { UZ = unit_of(a, L.tb, u); load_unit(a, UZ, Z, L); }
-        lds_barrier();
-        if (has2) quantize_unit<BITS>(a, U2, BX1, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
-        if (last1) quantize_unit<BITS>(a, U1, BX1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
-        if (!splitX) quantize_unit<BITS>(a, UX, BX, X, L, 0, sh_s, sh_y, sh_codes);
-        // advance the deferral pipeline
-        has2 = has1 && !last1;
-        if (has2) { U2 = U1; copy_regs(D2, D1); }
-        has1 = splitX;
-        if (has1) { U1 = UX; copy_regs(D1, X); }
-    }
-
-    // drain: a deferred last chunk first (its maximum may be awaited), then
-    // the waiting chunks
-    if (has1 && U1.c == U1.nc - 1) {
-        if (tid < D) {
-            const float m = gather_partials(a.part + (U1.id - U1.c) * D + tid, U1.nc, D, 0.0f, epoch, status);
-            __hip_atomic_store(a.fin + fin_row(a, U1) * D + tid, tagged(epoch, m), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            *scale_ptr(a, U1, tid) = put_scale<BITS>(sh_s, sh_y, QP_SLOT_R, D, tid, m);
+            slot = QP_SLOT_W;
         }
         lds_barrier();
-        quantize_unit<BITS>(a, U1, BX1, D1, L, QP_SLOT_R, sh_s, sh_y, sh_codes);
-        has1 = false;
-    }
-    if (has2) {
-        if (tid < D) {
-            const uint64_t *fin2 = a.fin + fin_row(a, U2) * D + tid;
-            put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin2, load_slot(fin2), epoch, status));
-        }
-        lds_barrier();
-        quantize_unit<BITS>(a, U2, BX1, D2, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
-    }
-    if (has1) {
-        if (tid < D) {
-            const uint64_t *fin1 = a.fin + fin_row(a, U1) * D + tid;
-            put_scale<BITS>(sh_s, sh_y, QP_SLOT_W, D, tid, slot_max(fin1, load_slot(fin1), epoch, status));
-        }
-        lds_barrier();
-        quantize_unit<BITS>(a, U1, BX1, D1, L, QP_SLOT_W, sh_s, sh_y, sh_codes);
+        quantize_unit<BITS>(a, U, B, X, L, slot, sh_s, sh_y, sh_codes);
     }
 
     // ---- the last work-group to finish advances the epoch for the next launch

@@ -294,11 +294,11 @@ int qp_setup(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
 
     // LDS regions (bytes, 16-aligned): block maxima [max_pack][D], scales and
     // reciprocals [max_pack + 2][D], the staging area for words or code rows
-    // (words at 2, 4, 7, 8 bits, and 2 bits only with an even number of 16-byte
-    // chunks per row), then the block-offset and unit-start tables.
+    // (words at 4, 7, 8 bits, code rows at 2, 3, 5, 6 bits; the kernel takes
+    // the same choice), then the block-offset and unit-start tables.
     {
         auto up16 = [](int64_t v) { return (int)((v + 15) / 16 * 16); };
-        const bool direct = bits == 4 || bits == 7 || bits == 8 || (bits == 2 && lpr % 2 == 0);
+        const bool direct = bits == 4 || bits == 7 || bits == 8;
         const int64_t stage = direct ? (int64_t)a.W * (T + 1) * 4 : (int64_t)T * (D >= 64 ? D + 4 : D);
         int o = 0;
         a.lds_max = o;   o += up16((int64_t)max_pack * D * 4);
