@@ -149,3 +149,34 @@ def test_kv_split_repeated_calls_alternating_shapes(V):
             torch.cuda.synchronize()
             for a, b in zip(got, ref):
                 assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, k.shape)
+
+
+def test_kv_block_with_as_many_chunks_as_resident_workgroups(V):
+    """The cooperative kernel's extreme case: after a one-unit block, a block of
+    exactly as many 128-row chunks as there are resident work-groups (the most
+    the host accepts), so it crosses a round boundary, for K and V in one
+    launch. A block of one chunk more is rejected before any launch."""
+    import re
+    _say("[kv max chunks]")
+    B, H, D, bits, T = 1, 1, 128, 4, 128
+    # the resident count, from the host's rejection of an oversized block
+    n_big = 8192
+    xb = torch.empty(B, n_big * T, H, D, dtype=torch.bfloat16, device=DEV)
+    caches = _caches(V, B, H, D, n_big * T, 1, bits)
+    with pytest.raises(V.VarqError) as ei:
+        V.quantize_pack_kv(xb, xb.clone(), [0, n_big * T], bits, *caches)
+    m = re.search(r"exceeds the (\d+) resident work-groups", str(ei.value))
+    assert m, str(ei.value)
+    G = int(m.group(1))
+    assert 0 < G < n_big
+    del xb, caches
+    g = torch.Generator().manual_seed(11)
+    off = [0, 64, 64 + G * T]
+    k = (torch.randn(B, off[-1], H, D, generator=g) * 2).to(torch.bfloat16)
+    v = torch.randn(B, off[-1], H, D, generator=g).to(torch.bfloat16)
+    _check(V, k, v, off, bits)
+    # one chunk more than resident work-groups: rejected
+    off2 = [0, 64, 64 + (G + 1) * T]
+    x2 = torch.zeros(B, off2[-1], H, D, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(V.VarqError):
+        V.quantize_pack_kv(x2, x2.clone(), off2, bits, *_caches(V, B, H, D, off2[-1], 2, bits))
