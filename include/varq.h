@@ -307,6 +307,18 @@ int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
                         void *out, int64_t so_b, int64_t so_l, int64_t so_h,
                         void *stream);
 
+/* Whether a quantize+pack call on `stream` since the previous check ended a
+ * cross-work-group wait by its time bound (the cooperative launch used when a
+ * block is longer than one work-group's rows). The kernel's waits end by
+ * construction; the bound only keeps a faulty device from hanging, and a wait
+ * cut short leaves that call's outputs invalid. Synchronizes `stream` (a
+ * hipStream_t; NULL = the null stream) and reads the status word of that
+ * stream's exchange scratch.
+ * Returns VARQ_OK (also when no such launch ran on the stream), or
+ * VARQ_ELAUNCH after a timed-out wait (the status is then cleared) or when the
+ * status cannot be read. */
+int varq_quantize_pack_check(void *stream);
+
 /* Text of the last error reported to the calling thread ("" if none). */
 const char *varq_last_error(void);
 

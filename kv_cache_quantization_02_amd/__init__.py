@@ -20,6 +20,7 @@ from .varq import (  # noqa: F401
     packed_attention,
     packed_attention_rope,
     quantize_pack,
+    quantize_pack_check,
     quantize_pack_grouped,
     quantize_pack_kv,
     unpack_dequant,

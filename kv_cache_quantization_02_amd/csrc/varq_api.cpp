@@ -673,6 +673,28 @@ int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
     return launch_status(varq::launch_dense_attention(a, D, static_cast<hipStream_t>(stream)), "bf16_attention");
 }
 
+int varq_quantize_pack_check(void *stream) {
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack_check: no current device");
+    uint32_t *sync = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        auto it = g_scratch.find({dev, st});
+        if (it != g_scratch.end()) sync = it->second.sync;
+    }
+    if (!sync) return VARQ_OK;   // no cooperative launch on this stream yet
+    uint32_t status = 0;
+    if (hipStreamSynchronize(st) != hipSuccess ||
+        hipMemcpy(&status, sync + 2, sizeof(status), hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(VARQ_ELAUNCH, "quantize_pack_check: cannot read the exchange status");
+    if (status == 0) return VARQ_OK;
+    if (hipMemset(sync + 2, 0, sizeof(status)) != hipSuccess)
+        return fail(VARQ_ELAUNCH, "quantize_pack_check: cannot clear the exchange status");
+    return fail(VARQ_ELAUNCH, "quantize_pack: a cross-work-group wait on this stream hit its time bound; "
+                              "outputs of the calls since the last check are not valid");
+}
+
 const char *varq_last_error(void) { return g_last_error.c_str(); }
 
 const char *varq_version(void) { return "varq-mi355x 0.1 (gfx950)"; }

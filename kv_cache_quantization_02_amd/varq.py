@@ -55,6 +55,7 @@ _SIGNATURES = {
     "varq_grouped_scale_count": (_i64, [_i32, _i32, _i64, _i32, _i32, _i32]),
     "varq_quantize_pack_grouped": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i32, _i32p, _i32,
                                           _i32, _vp, _i64, _vp, _i64, _vp]),
+    "varq_quantize_pack_check": (_i32, [_vp]),
     "varq_last_error": (ctypes.c_char_p, []),
     "varq_version": (ctypes.c_char_p, []),
 }
@@ -188,6 +189,14 @@ def quantize_pack_kv(k, v, group_offsets, bits, packed_k, scales_k, packed_v, sc
         B, H, D, L, off, G, bits, packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
         packed_k.shape[3], tok_start, scales_k.shape[2], group_start, _stream(stream, k.device)))
     return packed_k, scales_k, packed_v, scales_v
+
+
+def quantize_pack_check(device=None, stream=None):
+    """Raise VarqError if a quantize+pack call on the stream (default: the
+    current stream of `device`) since the previous check ended a
+    cross-work-group wait by its time bound; synchronizes that stream."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    _check(lib().varq_quantize_pack_check(_stream(stream, dev)))
 
 
 def frame_group_offsets(L, group_tokens, phase=0):

@@ -44,6 +44,7 @@ def _check(V, k_cpu, v_cpu, off, bits, k_dev=None, v_dev=None, tok_start=0, grou
     pk, sk, pv, sv = _caches(V, B, H, D, tok_start + L + extra_rows, group_start + G + extra_groups, bits)
     V.quantize_pack_kv(k_cpu.to(DEV) if k_dev is None else k_dev, v_cpu.to(DEV) if v_dev is None else v_dev,
                        off, bits, pk, sk, pv, sv, tok_start=tok_start, group_start=group_start)
+    V.quantize_pack_check()          # no cross-work-group wait hit its time bound
     torch.cuda.synchronize()
     for name, x, p, s in (("K", k_cpu, pk, sk), ("V", v_cpu, pv, sv)):
         w_ref, s_ref = O.quantize_pack(x.float().numpy(), off, bits)
@@ -146,6 +147,7 @@ def test_kv_split_repeated_calls_alternating_shapes(V):
             B, L, H, D = k.shape
             got = _caches(V, B, H, D, L, len(off) - 1, 4)
             V.quantize_pack_kv(k, v, off, 4, *got)
+            V.quantize_pack_check()
             torch.cuda.synchronize()
             for a, b in zip(got, ref):
                 assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, k.shape)
