@@ -298,39 +298,16 @@ def packed_attention(q, words_k, scales_k, words_v, scales_v, offsets, bits,
 
 
 def attention_error(o_test, o_ref_bf16, C):
-    """Normalised elementwise error |O_test - O_ref| / max(1, C) (max, mean), and
-    the raw max/mean absolute error."""
+    """The attention tolerance's error measure (a reading: the pages state no
+    tolerance, and the absolute bound alone is below the bf16 spacing of
+    outputs whose size exceeds 2): the elementwise |O_test - O_ref| divided by
+    max(1, C), where C = P|V^| is the size of the weighted sum behind each
+    output, reported as its max and mean, next to the raw max/mean absolute
+    error. Where C <= 1 the normalised error is the absolute error."""
     d = np.abs(np.asarray(o_test, dtype=np.float64) - np.asarray(o_ref_bf16, dtype=np.float64))
     e = d / np.maximum(1.0, C)
     return {"max_norm": float(e.max()), "mean_norm": float(e.mean()),
             "max_abs": float(d.max()), "mean_abs": float(d.mean())}
-
-
-# --------------------------------------------------------------------------
-# Grouping variants of project page Table 1 (per-tensor, per-block,
-# per-channel, channel x block), as quantize-dequantize in fp32
-# --------------------------------------------------------------------------
-
-def fake_quant(x, offsets, bits, per_channel=True) -> np.ndarray:
-    """Quantize then dequantize x [B, L, H, D] with one scale per (batch, head,
-    block) and, if per_channel, per channel as well. offsets=[0, L] removes the
-    block axis. Returns float32 [B, L, H, D] (bf16 values)."""
-    x = np.asarray(x, dtype=np.float32)
-    B, L, H, D = x.shape
-    off = _check_offsets(offsets, L)
-    qm = np.float32(qmax(bits))
-    out = np.empty_like(x)
-    for g in range(len(off) - 1):
-        xg = x[:, off[g]:off[g + 1]]                                  # [B, n, H, D]
-        a = np.abs(xg).max(axis=1, keepdims=True)                     # [B, 1, H, D]
-        if not per_channel:
-            a = a.max(axis=3, keepdims=True)                          # [B, 1, H, 1]
-        s = (a / qm).astype(np.float32)
-        safe = np.where(s == 0, np.float32(1), s)
-        r = np.where(s == 0, np.float32(0), np.divide(xg, safe, dtype=np.float32))
-        q = np.clip(np.rint(r), -qm, qm).astype(np.float32)
-        out[:, off[g]:off[g + 1]] = bf16_round_f32((q * s).astype(np.float32))
-    return out
 
 
 # --------------------------------------------------------------------------

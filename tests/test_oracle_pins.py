@@ -373,27 +373,39 @@ def test_attention_sampled_pairs_equal_full_decode():
 
 # ---------------------------------------------------------------- grouping semantics
 
-def test_table1_error_ordering_on_outlier_cache():
-    """Project page Table 1: relative Frobenius error falls per-tensor > per-block
-    > per-channel > channel x block. On the next-scale outlier generator the
-    same ordering holds for K and V at INT4."""
-    from synth import WORKLOADS, workload_inputs
-    wl = WORKLOADS["tiny"]
-    k, v, _ = workload_inputs(wl, seed=0)
-    for t in (k, v):
-        x = t.float().numpy()
-        L = x.shape[1]
-        errs = []
-        for offs, per_ch in (([0, L], False), (list(wl.offsets), False),
-                             ([0, L], True), (list(wl.offsets), True)):
-            xq = O.fake_quant(x, offs, 4, per_channel=per_ch)
-            errs.append(np.linalg.norm(xq - x) / np.linalg.norm(x))
-        assert errs[0] > errs[1] > errs[2] > errs[3], errs
-        # channel x block through fake_quant equals the real quantize/dequantize
-        w, s = O.quantize_pack(x, list(wl.offsets), 4)
-        deq = O.unpack_dequant(w, s, list(wl.offsets), x.shape[3], 4)
-        assert np.array_equal(deq.transpose(0, 2, 1, 3),
-                              O.fake_quant(x, list(wl.offsets), 4, per_channel=True))
+def test_attention_error_hand_worked():
+    """The tolerance measure on values worked out by hand: outputs whose C is
+    below 1 (floor 1: the error stays absolute), exactly 1, and above 1
+    (divided by C). d = [0.25, 0.5, 2, 6], max(1, C) = [1, 1, 4, 3] give
+    e = [0.25, 0.5, 0.5, 2]: max 2, mean 3.25 / 4 = 0.8125; raw max 6, mean
+    8.75 / 4 = 2.1875. Dividing by C without the floor (mean 0.875) or by
+    max(1, |O_ref|) (mean 1.0625) gives other means."""
+    o_test = np.array([[0.5, 2.0, -3.0, 10.0]])
+    o_ref = np.array([[0.25, 1.5, -1.0, 4.0]], dtype=np.float32)
+    C = np.array([[0.5, 1.0, 4.0, 3.0]])
+    e = O.attention_error(o_test, o_ref, C)
+    assert e == {"max_norm": 2.0, "mean_norm": 0.8125, "max_abs": 6.0, "mean_abs": 2.1875}
+    # a three-dimensional batch of such rows reduces over every element
+    e3 = O.attention_error(np.stack([o_test, o_ref.astype(np.float64)]), np.stack([o_ref, o_ref]),
+                           np.stack([C, C]))
+    assert e3["max_norm"] == 2.0 and e3["mean_norm"] == 0.8125 / 2 and e3["max_abs"] == 6.0
+
+
+def test_attention_conditioning_is_weighted_abs_sum():
+    """C = P|V^| by hand: two keys with logits 0 and ln 3 (sigma = 1, D = 1
+    would do, but the layout wants D of the cache: a one-channel query on an
+    8-channel head), so P = [1/4, 3/4]; V^ rows [2, -4] in channel 0 give
+    O = 1/4 * 2 + 3/4 * (-4) = -2.5 and C = 1/4 * 2 + 3/4 * 4 = 3.5."""
+    D = 8
+    q = np.zeros((1, 1, 1, D), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, 1, 2, D))
+    k[0, 0, 1, 0] = math.log(3.0)
+    v = np.zeros((1, 1, 2, D))
+    v[0, 0, :, 0] = [2.0, -4.0]
+    Ot, Ct, ob = O.attention_fp64(q, k, v, np.float32(1.0))
+    assert abs(Ot[0, 0, 0] - (-2.5)) < 1e-12 and abs(Ct[0, 0, 0] - 3.5) < 1e-12
+    assert ob[0, 0, 0] == np.float32(-2.5) and np.all(Ct[0, 0, 1:] == 0)
 
 
 def test_reduction_rejects_alternative_layouts():
