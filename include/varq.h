@@ -13,19 +13,21 @@
  *
  * Conventions for every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
- *    frees them and keeps no reference after the call returns. The only memory
- *    the library allocates is scratch it owns per (device, stream): the
+ *    frees them, keeps no reference after the call returns and allocates no
+ *    device memory of its own. Calls that may need device scratch (the
  *    cross-work-group exchange of quantize+pack for blocks longer than one
- *    work-group, and the partial results of attention launches split over KV
- *    ranges (both described at their entry points).
+ *    work-group, the partial results of attention launches split over KV
+ *    ranges) take a caller-owned `workspace` of at least the bytes that the
+ *    matching *_workspace query returns (NULL is accepted when it returns 0).
  *  - `group_offsets` is a HOST array of G+1 int32 prefix offsets
  *    0 = o_0 < o_1 < ... < o_G: block g covers tokens [o_g, o_{g+1}).
  *    G <= VARQ_MAX_GROUPS per call.
  *  - Strides are in elements. The channel (head_dim) stride is 1 ("BLHc"
  *    layout of the README's qkv_format: [batch, token, head, channel]).
- *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
- *    enqueues work on that stream and returns; results are ready when the
- *    stream reaches them.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every compute call
+ *    only enqueues work on that stream and returns; results are ready when the
+ *    stream reaches them. No call synchronizes the stream except
+ *    varq_quantize_pack_check, which exists to read a status back.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched and a negative varq_status is returned.
  *    varq_last_error() then describes the failure (per calling thread).
@@ -58,16 +60,22 @@ typedef enum varq_status {
     VARQ_EALIGN = -3,       /* pointer or stride not aligned as documented */
     VARQ_ECAPACITY = -4,    /* write or read range outside the preallocated cache */
     VARQ_ELAUNCH = -5,      /* the HIP runtime reported an error */
-    VARQ_EUNSUPPORTED = -6  /* valid request the kernels do not implement (e.g. head_dim) */
+    VARQ_EUNSUPPORTED = -6, /* valid request the kernels do not implement (e.g. head_dim) */
+    VARQ_EWORKSPACE = -7    /* workspace NULL or smaller than the workspace query's answer */
 } varq_status;
 
 #define VARQ_MAX_GROUPS 256
 
-/* Codes of `bits` bits per INT32 container: floor(32/bits); 0 if bits is not in 2..8. */
+/* Codes of `bits` bits per INT32 container: floor(32/bits); 0 if bits is not
+ * in 2..8. The project page's summary and Fig. 8 pack 2-8 bit codes into INT32
+ * containers without naming a layout; whole fields per word is this library's
+ * reading (it reproduces the Table 4 INT6 rows, which need 5 codes per word). */
 int varq_codes_per_word(int bits);
 
 /* INT32 words per (batch, head, token) row: ceil(head_dim / floor(32/bits));
- * 0 if bits is not in 2..8 or head_dim < 1. */
+ * 0 if bits is not in 2..8 or head_dim < 1. Packing runs along head_dim
+ * (project page Fig. 8 packs each token's codes; the per-row word count with a
+ * partly empty last word reproduces the Table 4 INT6 memory rows). */
 int varq_words_per_row(int head_dim, int bits);
 
 /*
@@ -98,14 +106,17 @@ int varq_cache_bytes(int B, int H, int head_dim, int64_t L_cap, int64_t G_cap, i
  * (tok_start+L_in > L_cap or group_start+G_in > G_cap), VARQ_EUNSUPPORTED (a
  * block of more 16384-element chunks than resident work-groups, or a token
  * stride or cache length beyond 32-bit byte offsets), VARQ_ELAUNCH.
- * Scratch: when some block is longer than one work-group's 16384 elements
- * (16384 / D token rows), its chunks exchange per-channel maxima through
- * device scratch that the library owns per (device, stream): 12 bytes of
- * launch state plus 8 bytes per (chunk, channel) and per (block, channel),
- * grown on demand with hipMalloc (after synchronizing that stream) and kept
- * until the process ends. Such launches are cooperative (every work-group
- * resident). Calls on one stream are ordered; calls on different streams use
- * different scratch.
+ * Workspace: when some block is longer than one work-group's 16384 elements
+ * (16384 / D token rows), its chunks exchange per-channel maxima through the
+ * caller's workspace (varq_quantize_pack_workspace gives the size: 16 bytes of
+ * launch state plus 8 bytes per (chunk, channel) and per (block, channel);
+ * otherwise the size is 0 and workspace may be NULL). The workspace must be
+ * zero-filled once before its first use; every launch leaves it valid for the
+ * next (each slot carries the tag of the launch that wrote it, and the launch
+ * state advances the tag), so it is then reused without clearing, by calls of
+ * any shape, as long as calls sharing it are ordered on one stream. Such
+ * launches are cooperative (every work-group resident); a cross-work-group wait
+ * is bounded in time and one cut short is reported by varq_quantize_pack_check.
  * Deterministic: the output does not depend on launch order or timing.
  */
 int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
@@ -113,7 +124,16 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
                        const int32_t *group_offsets, int G_in, int bits,
                        int32_t *packed, int64_t L_cap, int64_t tok_start,
                        float *scales, int64_t G_cap, int64_t group_start,
-                       void *stream);
+                       void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes that a quantize+pack call over n_tensors (1: varq_quantize_pack,
+ * 2: varq_quantize_pack_kv) tensors of this shape and block map needs, in
+ * *bytes: 0 when every block fits one work-group's rows. Pure host arithmetic.
+ * Errors: VARQ_EBITS, VARQ_EINVAL.
+ */
+int varq_quantize_pack_workspace(int B, int H, int D, int64_t L_in, const int32_t *group_offsets, int G_in,
+                                 int bits, int n_tensors, int64_t *bytes);
 
 /*
  * quantize+pack of K and V together (project page Fig. 8: the new block's K
@@ -123,8 +143,9 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
  * cache layout for both. k and v have strides of their own; packed_k/packed_v
  * and scales_k/scales_v are distinct buffers. Both tensors go through one
  * launch (the cooperative kernel when some block is longer than one
- * work-group's 16384 elements, with the scratch rules above counting the
- * chunks and blocks of both tensors).
+ * work-group's 16384 elements, with the workspace rules above counting the
+ * chunks and blocks of both tensors: varq_quantize_pack_workspace with
+ * n_tensors = 2).
  * Errors: those of varq_quantize_pack, for either tensor, and VARQ_EINVAL when
  * K and V share a cache buffer.
  */
@@ -134,7 +155,7 @@ int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_
                           const int32_t *group_offsets, int G_in, int bits,
                           int32_t *packed_k, float *scales_k, int32_t *packed_v, float *scales_v,
                           int64_t L_cap, int64_t tok_start, int64_t G_cap, int64_t group_start,
-                          void *stream);
+                          void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Pre-RoPE quantization (project page Appendix F / Table 7; Insight 03, Eq. 3):
@@ -151,8 +172,8 @@ int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_
  *
  * varq_packed_attention_rope: varq_packed_attention with every dequantized K
  * tile rotated before the scores; q must already be rotated (it is not
- * cached). Same arguments, errors and tolerance as varq_packed_attention,
- * plus VARQ_EINVAL for a NULL table and VARQ_EALIGN.
+ * cached). Same arguments, errors, workspace and tolerance as
+ * varq_packed_attention, plus VARQ_EINVAL for a NULL table and VARQ_EALIGN.
  */
 int varq_unpack_dequant_rope(const int32_t *packed, const float *scales,
                              int B, int H, int D, int64_t L_cap, int64_t G_cap, int64_t L,
@@ -168,7 +189,8 @@ int varq_packed_attention_rope(const void *q, int64_t sq_b, int64_t sq_l, int64_
                                const int32_t *group_offsets, int G, int bits,
                                float softmax_scale,
                                void *out, int64_t so_b, int64_t so_l, int64_t so_h,
-                               const float *rope_cos, const float *rope_sin, void *stream);
+                               const float *rope_cos, const float *rope_sin,
+                               void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Scale groupings (project page, grouping ablation Table 5 and error table
@@ -212,8 +234,9 @@ int64_t varq_grouped_scale_count(int mode, int B, int64_t L, int H, int D, int G
  *               BLOCK, TOKEN_HEAD, TOKEN and TENSOR the buffer first holds the
  *               groups' maxima while the call runs (stream-ordered).
  *  D            head_dim: a multiple of 8, 8 <= D <= 256.
- * CHANNEL_BLOCK and CHANNEL run varq_quantize_pack (its scratch rules apply);
- * the other groupings run three passes over x and allocate nothing.
+ * CHANNEL_BLOCK and CHANNEL run varq_quantize_pack (its workspace rules apply,
+ * with the table of the grouping: CHANNEL is one block [0, L)); the other
+ * groupings run three passes over x and need no workspace.
  * Errors: VARQ_EBITS, VARQ_EINVAL (unknown mode, bad sizes or table),
  * VARQ_EALIGN, VARQ_ECAPACITY (L > L_cap or n_scales too small),
  * VARQ_EUNSUPPORTED (B*L*H*W or the scale count beyond 2^31 - 1), VARQ_ELAUNCH.
@@ -223,7 +246,8 @@ int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_
                                int B, int H, int D, int64_t L,
                                int mode, const int32_t *group_offsets, int G, int bits,
                                int32_t *packed, int64_t L_cap,
-                               float *scales, int64_t n_scales, void *stream);
+                               float *scales, int64_t n_scales,
+                               void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Packed-KV attention (project page "Next-block prediction": a block attends to
@@ -244,15 +268,16 @@ int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_
  *               strides multiples of 4. Must not overlap q or the cache.
  * Errors: VARQ_EBITS, VARQ_EINVAL, VARQ_EALIGN, VARQ_ECAPACITY, VARQ_EUNSUPPORTED
  * (D not 64/128), VARQ_ELAUNCH.
- * Scratch: when (b, h, query tile) work-groups fill less than two rounds of the
- * device, the window's 64-token tiles run in up to 8 ranges (at least 8 tiles
- * each) and a second kernel merges the ranges' unnormalized outputs and
+ * Workspace: when (b, h, query tile) work-groups fill less than two rounds of
+ * the device, the window's 64-token tiles run in up to 8 ranges (at least 8
+ * tiles each) and a second kernel merges the ranges' unnormalized outputs and
  * (maximum, sum) pairs with log-sum-exp weights. The partials, S*B*H*Lq*(D+2)
- * fp32 for S ranges, live in device scratch the library owns per (device,
- * stream), grown on demand with hipMalloc (after synchronizing that stream)
- * and kept until the process ends. Calls on one stream are ordered; calls on
- * different streams use different scratch. The range count depends only on
- * the shapes and the device's compute-unit count.
+ * fp32 for S ranges, live in the caller's workspace
+ * (varq_packed_attention_workspace gives the size; 0 for one range, when
+ * workspace may be NULL). Its contents on entry do not matter: every launch
+ * writes each partial it reads. Calls sharing a workspace must be ordered on
+ * one stream. The range count depends only on the shapes and the current
+ * device's compute-unit count.
  */
 int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
                           int B, int H, int D, int64_t Lq,
@@ -262,7 +287,16 @@ int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
                           const int32_t *group_offsets, int G, int bits,
                           float softmax_scale,
                           void *out, int64_t so_b, int64_t so_l, int64_t so_h,
-                          void *stream);
+                          void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes of a packed (or bf16) attention call of this shape on the
+ * current device, in *bytes (0 when the window runs as one range). Host
+ * arithmetic plus a query of the device's compute-unit count.
+ * Errors: VARQ_EINVAL (bad sizes), VARQ_EUNSUPPORTED (D not 64/128),
+ * VARQ_ELAUNCH (no device).
+ */
+int varq_packed_attention_workspace(int B, int H, int D, int64_t Lq, int64_t L_kv, int64_t *bytes);
 
 /*
  * unpack+dequant (README "Memory-Efficient Runtime"; project page Fig. 8): the
@@ -297,27 +331,28 @@ int varq_unpack_dequant(const int32_t *packed, const float *scales,
  *               strides multiples of 4. Must not overlap q, k or v.
  * Errors: VARQ_EINVAL, VARQ_EALIGN, VARQ_ECAPACITY (L_kv > L_rows),
  * VARQ_EUNSUPPORTED (D not 64/128), VARQ_ELAUNCH.
- * Scratch and KV ranges as for varq_packed_attention (same plan for the same
- * shapes, so both paths compute in the same order).
+ * Workspace and KV ranges as for varq_packed_attention (same plan and the
+ * same varq_packed_attention_workspace size for the same shapes, so both paths
+ * compute in the same order).
  */
 int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
                         int B, int H, int D, int64_t Lq,
                         const void *k, const void *v, int64_t L_rows, int64_t L_kv,
                         float softmax_scale,
                         void *out, int64_t so_b, int64_t so_l, int64_t so_h,
-                        void *stream);
+                        void *workspace, int64_t workspace_bytes, void *stream);
 
-/* Whether a quantize+pack call on `stream` since the previous check ended a
- * cross-work-group wait by its time bound (the cooperative launch used when a
- * block is longer than one work-group's rows). The kernel's waits end by
- * construction; the bound only keeps a faulty device from hanging, and a wait
- * cut short leaves that call's outputs invalid. Synchronizes `stream` (a
- * hipStream_t; NULL = the null stream) and reads the status word of that
- * stream's exchange scratch.
- * Returns VARQ_OK (also when no such launch ran on the stream), or
+/* Whether a quantize+pack call that used `workspace` since the previous check
+ * ended a cross-work-group wait by its time bound (the cooperative launch used
+ * when a block is longer than one work-group's rows). The kernel's waits end
+ * by construction; the bound only keeps a faulty device from hanging, and a
+ * wait cut short leaves that call's outputs invalid. Synchronizes `stream` (a
+ * hipStream_t; NULL = the null stream; the stream the calls ran on) and reads
+ * the status word in the workspace's launch state.
+ * Returns VARQ_OK (also for a NULL workspace or one no such launch used), or
  * VARQ_ELAUNCH after a timed-out wait (the status is then cleared) or when the
  * status cannot be read. */
-int varq_quantize_pack_check(void *stream);
+int varq_quantize_pack_check(void *workspace, void *stream);
 
 /* Text of the last error reported to the calling thread ("" if none). */
 const char *varq_last_error(void);

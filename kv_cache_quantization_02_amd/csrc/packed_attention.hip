@@ -28,6 +28,7 @@
 // Only the last tile of the window masks tokens past it; only tiles that
 // contain a block boundary take the per-token scale path.
 #include "varq_device.h"
+#include "varq_tile_math.h"
 
 namespace varq {
 
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
             plane[r] = reinterpret_cast<const uint32_t *>((it_v[r] ? a.vd : a.kd) + (int64_t)bh * a.L_cap * D +
                                                           it_w[r] * CPW);
         else
-            plane[r] = (it_v[r] ? a.pv : a.pk) + ((int64_t)bh * W + it_w[r]) * a.L_cap + 4 * it_t4[r];
+            plane[r] = (it_v[r] ? a.pv : a.pk) + ((int64_t)bh * W + it_w[r]) * a.L_cap;
         sbase[r] = DENSE ? nullptr : (it_v[r] ? a.sv : a.sk) + (int64_t)bh * a.G_cap * D + it_w[r] * CPW;
     }
 
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
 #pragma unroll
         for (int r = 0; r < IPT; ++r) {
             if (!it_ok[r]) continue;
-            const uint4 v0 = *reinterpret_cast<const uint4 *>(plane[r] + n0);
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(plane[r] + attn_item_first_token(n0, it_t4[r], L_kv));
             P.wd[r][0] = v0.x; P.wd[r][1] = v0.y; P.wd[r][2] = v0.z; P.wd[r][3] = v0.w;
             if constexpr (SL) continue;
             const float *srow = sbase[r] + P.g * D;
@@ -215,8 +216,9 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         }
     };
 
-    // words of tile n0 (always in bounds: t + 4 <= L_cap) and, for a tile inside
-    // one block, that block's scales
+    // words of tile n0 (items past the window re-read its last 4-token group,
+    // so no load leaves the cache) and, for a tile inside one block, that
+    // block's scales
     auto prefetch = [&](Pref &P, int n0) {
         if constexpr (DENSE) {
             // 4 rows of 8 channels per item; rows past L_kv re-read the last

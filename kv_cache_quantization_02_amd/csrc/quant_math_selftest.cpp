@@ -1,5 +1,6 @@
 // quant_math_selftest.cpp - host-only exhaustive check of the scalar arithmetic
-// the gfx950 kernels use for codes (varq_quant_math.h).
+// the gfx950 kernels use for codes (varq_quant_math.h), and of the attention's
+// tile-load indices (varq_tile_math.h).
 //
 // For every positive finite bf16 absmax a and every bf16 x with |x| <= a, the
 // kernels' code for x under s = fp32(a / qmax) must equal rint(fl32(x / s))
@@ -14,6 +15,7 @@
 #include <vector>
 
 #include "varq_quant_math.h"
+#include "varq_tile_math.h"
 
 namespace {
 
@@ -82,6 +84,23 @@ long long varq_selftest_dequant(int bits, uint32_t lo16, uint32_t hi16) {
         }
     }
     return bad;
+}
+
+// Highest cache token that the packed attention's tile loads read for a window
+// of L_kv tokens (every tile of the window, every item of a tile), with the
+// kernel's own index function. Must stay below the cache capacity.
+long long varq_selftest_attn_max_token(int L_kv) {
+    if (L_kv < 1) return -1;
+    const int nt = (L_kv + varq::kAttnTileTokens - 1) / varq::kAttnTileTokens;
+    long long hi = -1;
+    for (int jt = 0; jt < nt; ++jt)
+        for (int t4 = 0; t4 < varq::kAttnTileTokens / varq::kAttnItemTokens; ++t4) {
+            const int t = varq::attn_item_first_token(jt * varq::kAttnTileTokens, t4, L_kv);
+            if (t % varq::kAttnItemTokens) return -2;          // 16-byte alignment lost
+            const long long last = (long long)t + varq::kAttnItemTokens - 1;
+            if (last > hi) hi = last;
+        }
+    return hi;
 }
 
 }  // extern "C"

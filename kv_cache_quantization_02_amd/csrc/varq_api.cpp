@@ -8,10 +8,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
-#include <utility>
 
 #include "../../include/varq.h"
 #include "varq_device.h"
@@ -79,74 +79,21 @@ int words_per_row(int D, int bits) {
     return (D + cpw - 1) / cpw;
 }
 
-// Device scratch for quantize+pack's cross-work-group exchange, per (device,
-// stream). `sync` (epoch, finished count, status) is allocated once and zeroed;
-// the kernel leaves the count at zero and advances the epoch. `slots` grows on
-// demand and is zeroed when allocated; afterwards every slot the kernel reads
-// carries the epoch of the launch that wrote it, so stale contents never pass
-// for current ones, whatever the shapes of earlier calls.
-struct Scratch {
-    uint32_t *sync = nullptr;
-    uint64_t *slots = nullptr;
-    size_t n_slots = 0;
-    float *attn = nullptr;      // attention partials of KV-split launches
-    size_t attn_bytes = 0;
-};
-std::mutex g_scratch_mu;
-std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+// Caller workspace of a split quantize+pack: launch state {epoch, finished
+// work-groups, timeout status, unused} (16 bytes), then 64-bit tagged slots:
+// per-unit partial maxima [n_units, D] and block maxima [T*B*H*G, D].
+constexpr int64_t kQpStateBytes = 16;
 
-int scratch_for(hipStream_t st, size_t n_slots, uint32_t **sync, uint64_t **slots) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack: no current device");
-    std::lock_guard<std::mutex> lk(g_scratch_mu);
-    Scratch &s = g_scratch[{dev, st}];
-    if (!s.sync) {
-        void *p = nullptr;
-        if (hipMalloc(&p, 4 * sizeof(uint32_t)) != hipSuccess || hipMemset(p, 0, 4 * sizeof(uint32_t)) != hipSuccess)
-            return fail(VARQ_ELAUNCH, "quantize_pack: scratch allocation failed");
-        s.sync = static_cast<uint32_t *>(p);
-    }
-    if (s.n_slots < n_slots) {
-        if (s.slots) {
-            // the old buffer may still be in use by work queued on this stream
-            if (hipStreamSynchronize(st) != hipSuccess || hipFree(s.slots) != hipSuccess)
-                return fail(VARQ_ELAUNCH, "quantize_pack: cannot release scratch");
-            s.slots = nullptr;
-            s.n_slots = 0;
-        }
-        void *p = nullptr;
-        if (hipMalloc(&p, n_slots * 8) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack: scratch allocation failed");
-        if (hipMemset(p, 0, n_slots * 8) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack: scratch clear failed");
-        s.slots = static_cast<uint64_t *>(p);
-        s.n_slots = n_slots;
-    }
-    *sync = s.sync;
-    *slots = s.slots;
-    return VARQ_OK;
+int64_t qp_workspace_bytes(int64_t n_units, int64_t bhg, int D) {
+    return kQpStateBytes + (n_units + bhg) * D * 8;
 }
 
-
-// Attention partials for a launch split over KV ranges, per (device, stream),
-// grown on demand (after synchronizing that stream) and kept until the
-// process ends. Every launch writes all the partials it reads.
-int attn_scratch_for(hipStream_t st, size_t bytes, float **p_out) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(VARQ_ELAUNCH, "packed_attention: no current device");
-    std::lock_guard<std::mutex> lk(g_scratch_mu);
-    Scratch &s = g_scratch[{dev, st}];
-    if (s.attn_bytes < bytes) {
-        if (s.attn) {
-            if (hipStreamSynchronize(st) != hipSuccess || hipFree(s.attn) != hipSuccess)
-                return fail(VARQ_ELAUNCH, "packed_attention: cannot release scratch");
-            s.attn = nullptr;
-            s.attn_bytes = 0;
-        }
-        void *p = nullptr;
-        if (hipMalloc(&p, bytes) != hipSuccess) return fail(VARQ_ELAUNCH, "packed_attention: scratch allocation failed");
-        s.attn = static_cast<float *>(p);
-        s.attn_bytes = bytes;
-    }
-    *p_out = s.attn;
+int check_workspace(const void *ws, int64_t have, int64_t need, const char *what) {
+    if (need == 0) return VARQ_OK;
+    if (ws == nullptr || have < need)
+        return fail(VARQ_EWORKSPACE, "%s: needs a workspace of %lld bytes (got %s%lld bytes)", what,
+                    (long long)need, ws ? "" : "NULL, ", (long long)have);
+    if (!aligned(ws, 16)) return fail(VARQ_EALIGN, "%s: workspace must be 16-byte aligned", what);
     return VARQ_OK;
 }
 
@@ -184,15 +131,30 @@ int plan_kv_splits(int64_t wgs, int nt, int per_cu) {
     return best;
 }
 
+// KV ranges planned for an attention launch of this shape on the current
+// device, and the partials workspace they need (0 for one range).
+int attn_ranges(int B, int H, int D, int64_t Lq, int64_t L_kv, int *S, int64_t *ws_bytes) {
+    const int qtile = varq::attention_q_tile();
+    const int64_t n_qtiles = (Lq + qtile - 1) / qtile;
+    const int nt = (int)((L_kv + 63) / 64);
+    *S = plan_kv_splits(n_qtiles * B * H, nt, D == 64 ? 2 : 1);
+    *ws_bytes = *S == 1 ? 0 : (int64_t)*S * B * H * Lq * (D + 2) * (int64_t)sizeof(float);
+    return VARQ_OK;
+}
+
 // KV ranges of an attention launch (a.off, a.L_kv, a.Lq, a.B, a.H and
-// a.n_qtiles set): one range, or the planned split with its partials scratch.
-int setup_kv_ranges(varq::AttnArgs &a, int D, void *stream) {
+// a.n_qtiles set): one range, or the planned split with its partials in the
+// caller's workspace.
+int setup_kv_ranges(varq::AttnArgs &a, int D, void *ws, int64_t ws_bytes, const char *what) {
     const int nt = (int)((a.L_kv + 63) / 64);
     a.kv_splits = 1;
     a.split_t0[0] = 0;
     a.split_t0[1] = nt;
     a.split_g0[0] = 0;
-    const int S = plan_kv_splits((int64_t)a.n_qtiles * a.B * a.H, nt, D == 64 ? 2 : 1);
+    int S = 1;
+    int64_t need = 0;
+    attn_ranges(a.B, a.H, D, a.Lq, a.L_kv, &S, &need);
+    if (int r = check_workspace(ws, ws_bytes, need, what)) return r;
     if (S == 1) return VARQ_OK;
     a.kv_splits = S;
     int g = 0;
@@ -203,11 +165,61 @@ int setup_kv_ranges(varq::AttnArgs &a, int D, void *stream) {
     }
     a.split_t0[S] = nt;
     const size_t rows = (size_t)S * a.B * a.H * a.Lq;
-    float *part = nullptr;
-    if (int r = attn_scratch_for(static_cast<hipStream_t>(stream), rows * (D + 2) * sizeof(float), &part)) return r;
+    float *part = static_cast<float *>(ws);
     a.part_o = part;
     a.part_ml = part + rows * D;
     return VARQ_OK;
+}
+
+// Work units of quantize+pack over one (batch, head): at most T rows each (T *
+// D = the elements one work-group holds). A block longer than T is cut into
+// chunks; shorter consecutive blocks are packed together, up to T rows and
+// quant_pack_max_pack() blocks per unit.
+struct QpPlan {
+    int T = 0, tl = 0;      // rows per unit and ceil(log2 T)
+    int units = 0;          // units per (batch, head)
+    int max_nc = 1;         // most chunks of one block
+    int32_t unit_start[VARQ_MAX_GROUPS + 1];
+};
+
+void qp_plan(const int32_t *off, int G, int D, QpPlan &p) {
+    const int lpr = D / 8;
+    p.T = (256 / lpr) * 8;
+    p.tl = 0;
+    while ((1 << p.tl) < p.T) ++p.tl;
+    const int max_pack = varq::quant_pack_max_pack();
+    int units = 0, pack_rows = 0, pack_blocks = 0;
+    bool in_pack = false;
+    p.max_nc = 1;
+    for (int g = 0; g < G; ++g) {
+        const int n = off[g + 1] - off[g];
+        if (n > p.T) {
+            const int nc = (n + p.T - 1) / p.T;
+            p.unit_start[g] = units;
+            units += nc;
+            p.max_nc = std::max(p.max_nc, nc);
+            in_pack = false;
+        } else if (in_pack && pack_rows + n <= p.T && pack_blocks < max_pack) {
+            p.unit_start[g] = units - 1;
+            pack_rows += n;
+            ++pack_blocks;
+        } else {
+            p.unit_start[g] = units++;
+            in_pack = true;
+            pack_rows = n;
+            pack_blocks = 1;
+        }
+    }
+    p.unit_start[G] = units;
+    p.units = units;
+}
+
+// Workspace of a quantize+pack launch over n_tensors tensors (0 when no block
+// spans several units).
+int64_t qp_plan_workspace(const QpPlan &p, int n_tensors, int B, int H, int G, int D) {
+    if (p.max_nc <= 1) return 0;
+    const int64_t n_units = (int64_t)n_tensors * B * H * p.units;
+    return qp_workspace_bytes(n_units, (int64_t)n_tensors * B * H * G, D);
 }
 
 // Validates one tensor's quantize+pack arguments and fills the launch
@@ -246,46 +258,23 @@ int qp_setup(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
     a.L_cap = L_cap; a.tok_start = tok_start; a.G_cap = G_cap; a.group_start = group_start;
     a.B = B; a.H = H; a.D = D; a.G = G_in;
     a.W = words_per_row(D, bits);
-    // Units of at most T rows (T * D = the elements one work-group holds): a
-    // block longer than T is cut into chunks; shorter consecutive blocks are
-    // packed together, up to T rows and quant_pack_max_pack() blocks per unit.
-    const int lpr = D / 8;
-    const int T = (256 / lpr) * 8;
-    int tl = 0;
-    while ((1 << tl) < T) ++tl;
+    QpPlan p;
+    qp_plan(group_offsets, G_in, D, p);
+    const int T = p.T;
     a.chunk_rows = T;
-    a.rows_log2 = tl;
+    a.rows_log2 = p.tl;
     const int max_pack = varq::quant_pack_max_pack();
-    int units = 0, max_nc = 1, pack_rows = 0, pack_blocks = 0;
-    bool in_pack = false;
-    for (int g = 0; g < G_in; ++g) {
+    for (int g = 0; g <= G_in; ++g) {
         a.off[g] = group_offsets[g];
-        const int n = group_offsets[g + 1] - group_offsets[g];
-        if (n > T) {
-            const int nc = (n + T - 1) / T;
-            a.unit_start[g] = units;
-            units += nc;
-            max_nc = std::max(max_nc, nc);
-            in_pack = false;
-        } else if (in_pack && pack_rows + n <= T && pack_blocks < max_pack) {
-            a.unit_start[g] = units - 1;
-            pack_rows += n;
-            ++pack_blocks;
-        } else {
-            a.unit_start[g] = units++;
-            in_pack = true;
-            pack_rows = n;
-            pack_blocks = 1;
-        }
+        a.unit_start[g] = p.unit_start[g];
     }
+    const int units = p.units, max_nc = p.max_nc;
     // the kernel addresses a unit's rows and a (batch, head)'s word planes with
     // 32-bit byte offsets
     if ((int64_t)T * sx_l * 2 >= ((int64_t)1 << 31) || (int64_t)a.W * L_cap * 4 >= ((int64_t)1 << 31))
         return fail(VARQ_EUNSUPPORTED,
                     "quantize_pack: token stride %lld or cache length %lld too large for 32-bit offsets",
                     (long long)sx_l, (long long)L_cap);
-    a.off[G_in] = group_offsets[G_in];
-    a.unit_start[G_in] = units;
     a.units_per_bh = units;
     a.n_units = (int64_t)B * H * units;
     a.n_units_one = a.n_units;
@@ -313,11 +302,14 @@ int qp_setup(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
 }
 
 // Launches a prepared quantize+pack (one tensor, or two whose units follow
-// each other in one non-split launch).
-int qp_launch(varq::QuantPackArgs &a, int bits, bool split, int max_nc, void *stream) {
+// each other in one launch). A launch with blocks longer than one unit
+// exchanges block maxima through the caller's workspace.
+int qp_launch(varq::QuantPackArgs &a, int bits, bool split, int max_nc, void *ws, int64_t ws_bytes, void *stream) {
     const int D = a.D;
     int grid = 0;
     if (split) {
+        const int64_t bhg = (int64_t)(a.x2 ? 2 : 1) * a.B * a.H * a.G;
+        if (int r = check_workspace(ws, ws_bytes, qp_workspace_bytes(a.n_units, bhg, D), "quantize_pack")) return r;
         const int resident = varq::quant_pack_resident_blocks(bits, a.lds_bytes);
         if (resident <= 0) return fail(VARQ_ELAUNCH, "quantize_pack: cannot query the device occupancy");
         grid = (int)std::min<int64_t>(a.n_units, resident);
@@ -326,14 +318,10 @@ int qp_launch(varq::QuantPackArgs &a, int bits, bool split, int max_nc, void *st
         if (max_nc > grid)
             return fail(VARQ_EUNSUPPORTED, "quantize_pack: a block of %d chunks exceeds the %d resident work-groups",
                         max_nc, grid);
-        const size_t bhg = (size_t)(a.x2 ? 2 : 1) * a.B * a.H * a.G;
-        uint32_t *sync = nullptr;
-        uint64_t *slots = nullptr;
-        if (int r = scratch_for(static_cast<hipStream_t>(stream), ((size_t)a.n_units + bhg) * D, &sync, &slots))
-            return r;
-        a.sync = sync;
-        a.part = slots;
-        a.fin = slots + (size_t)a.n_units * D;
+        char *base = static_cast<char *>(ws);
+        a.sync = reinterpret_cast<uint32_t *>(base);
+        a.part = reinterpret_cast<uint64_t *>(base + kQpStateBytes);
+        a.fin = a.part + (size_t)a.n_units * D;
     } else {
         // whole blocks only: one work-group per unit
         grid = (int)std::min<int64_t>(a.n_units, (int64_t)1 << 30);
@@ -341,7 +329,6 @@ int qp_launch(varq::QuantPackArgs &a, int bits, bool split, int max_nc, void *st
     return launch_status(varq::launch_quant_pack(a, bits, grid, split, static_cast<hipStream_t>(stream)),
                          "quantize_pack");
 }
-
 
 }  // namespace
 
@@ -371,7 +358,7 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
                        const int32_t *group_offsets, int G_in, int bits,
                        int32_t *packed, int64_t L_cap, int64_t tok_start,
                        float *scales, int64_t G_cap, int64_t group_start,
-                       void *stream) {
+                       void *workspace, int64_t workspace_bytes, void *stream) {
     varq::QuantPackArgs a;
     bool empty = false, split = false;
     int max_nc = 1;
@@ -379,7 +366,26 @@ int varq_quantize_pack(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
                          scales, G_cap, group_start, a, &empty, &split, &max_nc))
         return r;
     if (empty) return ok();
-    return qp_launch(a, bits, split, max_nc, stream);
+    return qp_launch(a, bits, split, max_nc, workspace, workspace_bytes, stream);
+}
+
+int varq_quantize_pack_workspace(int B, int H, int D, int64_t L_in, const int32_t *group_offsets, int G_in,
+                                 int bits, int n_tensors, int64_t *bytes) {
+    if (int r = check_bits(bits)) return r;
+    if (!bytes) return fail(VARQ_EINVAL, "quantize_pack_workspace: bytes is NULL");
+    if (n_tensors != 1 && n_tensors != 2)
+        return fail(VARQ_EINVAL, "quantize_pack_workspace: n_tensors must be 1 or 2 (got %d)", n_tensors);
+    if (B < 1 || H < 1) return fail(VARQ_EINVAL, "quantize_pack_workspace: B=%d H=%d must be >= 1", B, H);
+    if (D < 8 || D > 256 || D % 8 != 0)
+        return fail(VARQ_EINVAL, "quantize_pack_workspace: head_dim %d must be a multiple of 8 in 8..256", D);
+    if (L_in < 0) return fail(VARQ_EINVAL, "quantize_pack_workspace: L_in=%lld < 0", (long long)L_in);
+    *bytes = 0;
+    if (L_in == 0 && G_in == 0) return ok();
+    if (int r = check_offsets(group_offsets, G_in, L_in, "quantize_pack_workspace")) return r;
+    QpPlan p;
+    qp_plan(group_offsets, G_in, D, p);
+    *bytes = qp_plan_workspace(p, n_tensors, B, H, G_in, D);
+    return ok();
 }
 
 int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_h,
@@ -388,7 +394,7 @@ int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_
                           const int32_t *group_offsets, int G_in, int bits,
                           int32_t *packed_k, float *scales_k, int32_t *packed_v, float *scales_v,
                           int64_t L_cap, int64_t tok_start, int64_t G_cap, int64_t group_start,
-                          void *stream) {
+                          void *workspace, int64_t workspace_bytes, void *stream) {
     varq::QuantPackArgs a, av;
     bool empty = false, split = false;
     int max_nc = 1;
@@ -406,7 +412,7 @@ int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_
     a.packed2 = av.packed;
     a.scales2 = av.scales;
     a.n_units = 2 * a.n_units_one;
-    return qp_launch(a, bits, split, max_nc, stream);
+    return qp_launch(a, bits, split, max_nc, workspace, workspace_bytes, stream);
 }
 
 int64_t varq_grouped_scale_count(int mode, int B, int64_t L, int H, int D, int G) {
@@ -426,7 +432,8 @@ int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_
                                int B, int H, int D, int64_t L,
                                int mode, const int32_t *group_offsets, int G, int bits,
                                int32_t *packed, int64_t L_cap,
-                               float *scales, int64_t n_scales, void *stream) {
+                               float *scales, int64_t n_scales,
+                               void *workspace, int64_t workspace_bytes, void *stream) {
     if (int r = check_bits(bits)) return r;
     if (mode < VARQ_GROUP_CHANNEL_BLOCK || mode > VARQ_GROUP_TENSOR)
         return fail(VARQ_EINVAL, "quantize_pack_grouped: unknown grouping %d", mode);
@@ -441,11 +448,11 @@ int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_
                     (long long)n_scales, (long long)count, mode);
     if (mode == VARQ_GROUP_CHANNEL_BLOCK)
         return varq_quantize_pack(x, sx_b, sx_l, sx_h, B, H, D, L, group_offsets, G, bits, packed, L_cap, 0,
-                                  scales, G, 0, stream);
+                                  scales, G, 0, workspace, workspace_bytes, stream);
     if (mode == VARQ_GROUP_CHANNEL) {
         const int32_t whole[2] = {0, (int32_t)L};
         return varq_quantize_pack(x, sx_b, sx_l, sx_h, B, H, D, L, whole, 1, bits, packed, L_cap, 0,
-                                  scales, 1, 0, stream);
+                                  scales, 1, 0, workspace, workspace_bytes, stream);
     }
     if (!x || !packed || !scales) return fail(VARQ_EINVAL, "quantize_pack_grouped: NULL tensor pointer");
     if (!aligned(x, 16) || sx_b % 8 || sx_l % 8 || sx_h % 8)
@@ -543,7 +550,7 @@ int packed_attention_impl(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
                           const int32_t *group_offsets, int G, int bits,
                           float softmax_scale,
                           void *out, int64_t so_b, int64_t so_l, int64_t so_h,
-                          const float *rcos, const float *rsin, void *stream) {
+                          const float *rcos, const float *rsin, void *ws, int64_t ws_bytes, void *stream) {
     if (int r = check_bits(bits)) return r;
     if (B < 1 || H < 1) return fail(VARQ_EINVAL, "packed_attention: B=%d H=%d must be >= 1", B, H);
     if (D != 64 && D != 128)
@@ -591,7 +598,7 @@ int packed_attention_impl(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
     a.rcos = rcos; a.rsin = rsin;
     for (int g = 0; g <= G; ++g) a.off[g] = group_offsets[g];
     // an under-filled grid runs its KV tiles in ranges, merged afterwards
-    if (int r = setup_kv_ranges(a, D, stream)) return r;
+    if (int r = setup_kv_ranges(a, D, ws, ws_bytes, "packed_attention")) return r;
     return launch_status(varq::launch_packed_attention(a, D, bits, static_cast<hipStream_t>(stream)),
                          "packed_attention");
 }
@@ -606,10 +613,25 @@ int varq_packed_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
                           const int32_t *group_offsets, int G, int bits,
                           float softmax_scale,
                           void *out, int64_t so_b, int64_t so_l, int64_t so_h,
-                          void *stream) {
+                          void *workspace, int64_t workspace_bytes, void *stream) {
     return packed_attention_impl(q, sq_b, sq_l, sq_h, B, H, D, Lq, packed_k, scales_k, packed_v, scales_v,
                                  L_cap, G_cap, L_kv, group_offsets, G, bits, softmax_scale, out, so_b, so_l, so_h,
-                                 nullptr, nullptr, stream);
+                                 nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int varq_packed_attention_workspace(int B, int H, int D, int64_t Lq, int64_t L_kv, int64_t *bytes) {
+    if (!bytes) return fail(VARQ_EINVAL, "packed_attention_workspace: bytes is NULL");
+    if (B < 1 || H < 1 || Lq < 0 || L_kv < 0)
+        return fail(VARQ_EINVAL, "packed_attention_workspace: bad sizes (B=%d H=%d Lq=%lld L_kv=%lld)", B, H,
+                    (long long)Lq, (long long)L_kv);
+    if (D != 64 && D != 128)
+        return fail(VARQ_EUNSUPPORTED, "packed_attention_workspace: head_dim %d not implemented (64 or 128)", D);
+    *bytes = 0;
+    if (Lq == 0 || L_kv == 0) return ok();
+    if (device_cus() <= 0) return fail(VARQ_ELAUNCH, "packed_attention_workspace: no current device");
+    int S = 1;
+    attn_ranges(B, H, D, Lq, L_kv, &S, bytes);
+    return ok();
 }
 
 int varq_packed_attention_rope(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
@@ -620,11 +642,12 @@ int varq_packed_attention_rope(const void *q, int64_t sq_b, int64_t sq_l, int64_
                                const int32_t *group_offsets, int G, int bits,
                                float softmax_scale,
                                void *out, int64_t so_b, int64_t so_l, int64_t so_h,
-                               const float *rope_cos, const float *rope_sin, void *stream) {
+                               const float *rope_cos, const float *rope_sin,
+                               void *workspace, int64_t workspace_bytes, void *stream) {
     if (!rope_cos || !rope_sin) return fail(VARQ_EINVAL, "packed_attention_rope: NULL rope table");
     return packed_attention_impl(q, sq_b, sq_l, sq_h, B, H, D, Lq, packed_k, scales_k, packed_v, scales_v,
                                  L_cap, G_cap, L_kv, group_offsets, G, bits, softmax_scale, out, so_b, so_l, so_h,
-                                 rope_cos, rope_sin, stream);
+                                 rope_cos, rope_sin, workspace, workspace_bytes, stream);
 }
 
 int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
@@ -632,7 +655,7 @@ int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
                         const void *k, const void *v, int64_t L_rows, int64_t L_kv,
                         float softmax_scale,
                         void *out, int64_t so_b, int64_t so_l, int64_t so_h,
-                        void *stream) {
+                        void *workspace, int64_t workspace_bytes, void *stream) {
     if (B < 1 || H < 1) return fail(VARQ_EINVAL, "bf16_attention: B=%d H=%d must be >= 1", B, H);
     if (D != 64 && D != 128)
         return fail(VARQ_EUNSUPPORTED, "bf16_attention: head_dim %d not implemented (64 or 128)", D);
@@ -669,29 +692,23 @@ int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
     a.off[0] = 0;
     a.off[1] = (int32_t)L_kv;
-    if (int r = setup_kv_ranges(a, D, stream)) return r;
+    if (int r = setup_kv_ranges(a, D, workspace, workspace_bytes, "bf16_attention")) return r;
     return launch_status(varq::launch_dense_attention(a, D, static_cast<hipStream_t>(stream)), "bf16_attention");
 }
 
-int varq_quantize_pack_check(void *stream) {
+int varq_quantize_pack_check(void *workspace, void *stream) {
+    if (!workspace) return ok();
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack_check: no current device");
-    uint32_t *sync = nullptr;
-    {
-        std::lock_guard<std::mutex> lk(g_scratch_mu);
-        auto it = g_scratch.find({dev, st});
-        if (it != g_scratch.end()) sync = it->second.sync;
-    }
-    if (!sync) return VARQ_OK;   // no cooperative launch on this stream yet
+    uint32_t *status_word = static_cast<uint32_t *>(workspace) + 2;     // launch state {epoch, finished, status}
     uint32_t status = 0;
     if (hipStreamSynchronize(st) != hipSuccess ||
-        hipMemcpy(&status, sync + 2, sizeof(status), hipMemcpyDeviceToHost) != hipSuccess)
+        hipMemcpy(&status, status_word, sizeof(status), hipMemcpyDeviceToHost) != hipSuccess)
         return fail(VARQ_ELAUNCH, "quantize_pack_check: cannot read the exchange status");
-    if (status == 0) return VARQ_OK;
-    if (hipMemset(sync + 2, 0, sizeof(status)) != hipSuccess)
+    if (status == 0) return ok();
+    const uint32_t zero = 0;
+    if (hipMemcpy(status_word, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
         return fail(VARQ_ELAUNCH, "quantize_pack_check: cannot clear the exchange status");
-    return fail(VARQ_ELAUNCH, "quantize_pack: a cross-work-group wait on this stream hit its time bound; "
+    return fail(VARQ_ELAUNCH, "quantize_pack: a cross-work-group wait in this workspace hit its time bound; "
                               "outputs of the calls since the last check are not valid");
 }
 

@@ -3,7 +3,10 @@
 Each function marshals torch tensors into the C ABI's pointers, strides and
 stream and calls the entry point of the same name (without the ``varq_``
 prefix). All computation happens in the gfx950 kernels; if the library is not
-built, every call raises. PyTorch supplies device memory and streams only.
+built, every call raises. PyTorch supplies device memory and streams only:
+the workspaces that some calls need are torch tensors, sized by the library's
+workspace queries and kept here per (device, stream) unless the caller passes
+one.
 """
 
 from __future__ import annotations
@@ -20,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libvarq.so")
 
 VARQ_OK = 0
 STATUS_NAMES = {0: "VARQ_OK", -1: "VARQ_EINVAL", -2: "VARQ_EBITS", -3: "VARQ_EALIGN",
-                -4: "VARQ_ECAPACITY", -5: "VARQ_ELAUNCH", -6: "VARQ_EUNSUPPORTED"}
+                -4: "VARQ_ECAPACITY", -5: "VARQ_ELAUNCH", -6: "VARQ_EUNSUPPORTED", -7: "VARQ_EWORKSPACE"}
 MAX_GROUPS = 256
 
 _lib = None
@@ -37,25 +40,28 @@ _SIGNATURES = {
     "varq_words_per_row": (_i32, [_i32, _i32]),
     "varq_cache_bytes": (_i32, [_i32, _i32, _i32, _i64, _i64, _i32, _i64p, _i64p]),
     "varq_quantize_pack": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i32p, _i32, _i32,
-                                  _vp, _i64, _i64, _vp, _i64, _i64, _vp]),
+                                  _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "varq_quantize_pack_workspace": (_i32, [_i32, _i32, _i32, _i64, _i32p, _i32, _i32, _i32, _i64p]),
     "varq_quantize_pack_kv": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64,
-                                     _i32p, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]),
+                                     _i32p, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                     _vp, _i64, _vp]),
     "varq_packed_attention": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64,
                                      _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32p, _i32, _i32,
-                                     _f32, _vp, _i64, _i64, _i64, _vp]),
+                                     _f32, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
+    "varq_packed_attention_workspace": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64p]),
     "varq_unpack_dequant": (_i32, [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32p, _i32, _i32,
                                    _vp, _vp]),
     "varq_bf16_attention": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _vp, _vp, _i64, _i64,
-                                   _f32, _vp, _i64, _i64, _i64, _vp]),
+                                   _f32, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "varq_unpack_dequant_rope": (_i32, [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32p, _i32, _i32,
                                         _vp, _vp, _vp, _vp]),
     "varq_packed_attention_rope": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64,
                                           _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32p, _i32, _i32,
-                                          _f32, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+                                          _f32, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
     "varq_grouped_scale_count": (_i64, [_i32, _i32, _i64, _i32, _i32, _i32]),
     "varq_quantize_pack_grouped": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i32, _i32p, _i32,
-                                          _i32, _vp, _i64, _vp, _i64, _vp]),
-    "varq_quantize_pack_check": (_i32, [_vp]),
+                                          _i32, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "varq_quantize_pack_check": (_i32, [_vp, _vp]),
     "varq_last_error": (ctypes.c_char_p, []),
     "varq_version": (ctypes.c_char_p, []),
 }
@@ -104,6 +110,60 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be a CUDA {dtype} tensor")
 
 
+# Workspaces kept per (device, stream, kind): "qp" (quantize+pack exchange;
+# zero-filled when allocated, then left to the library, which keeps it valid
+# from call to call) and "attn" (attention partials; contents irrelevant).
+_WS = {}
+
+
+def _stream_obj(stream, device):
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def get_workspace(kind, nbytes, device, stream=None):
+    """A cached workspace tensor of at least nbytes for calls of `kind` on
+    `stream` (default: the device's current stream), or None if nbytes is 0.
+    Growing allocates a new zero-filled tensor on that stream."""
+    if nbytes <= 0:
+        return None
+    device = torch.device(device)
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    st = _stream_obj(stream, device)
+    key = (device.index, st.cuda_stream, kind)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(st):
+            ws = torch.zeros(int(nbytes), dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def _ws_args(ws):
+    """(pointer, bytes) of a workspace tensor or None."""
+    if ws is None:
+        return None, 0
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError("workspace must be a contiguous CUDA tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def quantize_pack_workspace_bytes(B, H, D, group_offsets, bits, n_tensors=1):
+    """Workspace bytes of a quantize+pack call (0 when every block fits one work-group)."""
+    off, G = _offsets(group_offsets)
+    n = ctypes.c_int64()
+    _check(lib().varq_quantize_pack_workspace(B, H, D, int(group_offsets[-1]), off, G, bits, n_tensors,
+                                              ctypes.byref(n)))
+    return n.value
+
+
+def attention_workspace_bytes(B, H, D, Lq, L_kv):
+    """Workspace bytes of a packed (or bf16) attention call on the current device."""
+    n = ctypes.c_int64()
+    _check(lib().varq_packed_attention_workspace(B, H, D, Lq, L_kv, ctypes.byref(n)))
+    return n.value
+
+
 def last_error() -> str:
     return lib().varq_last_error().decode()
 
@@ -144,10 +204,12 @@ def alloc_cache(B, H, head_dim, L_cap, G_cap, bits, device="cuda"):
     return packed, scales
 
 
-def quantize_pack(x, group_offsets, bits, packed, scales, tok_start=0, group_start=0, stream=None):
+def quantize_pack(x, group_offsets, bits, packed, scales, tok_start=0, group_start=0, stream=None,
+                  workspace=None):
     """x bf16 [B, L_in, H, D] (channel stride 1) -> rows [tok_start, tok_start+L_in)
     of `packed` [B, H, W, L_cap] and slots [group_start, group_start+G_in) of
-    `scales` [B, H, G_cap, D]."""
+    `scales` [B, H, G_cap, D]. `workspace`: a zero-filled (once) uint8 tensor
+    of at least quantize_pack_workspace_bytes(); default: the stream's cached one."""
     _need(x, torch.bfloat16, "x")
     _need(packed, torch.int32, "packed")
     _need(scales, torch.float32, "scales")
@@ -157,18 +219,21 @@ def quantize_pack(x, group_offsets, bits, packed, scales, tok_start=0, group_sta
         raise ValueError("packed and scales must be contiguous")
     B, L, H, D = x.shape
     off, G = _offsets(group_offsets)
+    if workspace is None and L > 0:
+        workspace = get_workspace("qp", quantize_pack_workspace_bytes(B, H, D, group_offsets, bits, 1),
+                                           x.device, stream)
+    wp, wb = _ws_args(workspace)
     _check(lib().varq_quantize_pack(
         x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, H, D, L, off, G, bits,
         packed.data_ptr(), packed.shape[3], tok_start, scales.data_ptr(), scales.shape[2],
-        group_start, _stream(stream, x.device)))
+        group_start, wp, wb, _stream(stream, x.device)))
     return packed, scales
 
 
 def quantize_pack_kv(k, v, group_offsets, bits, packed_k, scales_k, packed_v, scales_v,
-                     tok_start=0, group_start=0, stream=None):
+                     tok_start=0, group_start=0, stream=None, workspace=None):
     """quantize_pack of k and of v (same shape and block map, each bf16
-    [B, L_in, H, D] with its own strides) into their own caches, in one launch
-    when every block fits one work-group."""
+    [B, L_in, H, D] with its own strides) into their own caches, in one launch."""
     for t, n in ((k, "k"), (v, "v")):
         _need(t, torch.bfloat16, n)
         if t.dim() != 4 or t.stride(3) != 1:
@@ -184,19 +249,29 @@ def quantize_pack_kv(k, v, group_offsets, bits, packed_k, scales_k, packed_v, sc
         raise ValueError("K and V caches must have one layout")
     B, L, H, D = k.shape
     off, G = _offsets(group_offsets)
+    if workspace is None and L > 0:
+        workspace = get_workspace("qp", quantize_pack_workspace_bytes(B, H, D, group_offsets, bits, 2),
+                                           k.device, stream)
+    wp, wb = _ws_args(workspace)
     _check(lib().varq_quantize_pack_kv(
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2), v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
         B, H, D, L, off, G, bits, packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
-        packed_k.shape[3], tok_start, scales_k.shape[2], group_start, _stream(stream, k.device)))
+        packed_k.shape[3], tok_start, scales_k.shape[2], group_start, wp, wb, _stream(stream, k.device)))
     return packed_k, scales_k, packed_v, scales_v
 
 
-def quantize_pack_check(device=None, stream=None):
-    """Raise VarqError if a quantize+pack call on the stream (default: the
-    current stream of `device`) since the previous check ended a
-    cross-work-group wait by its time bound; synchronizes that stream."""
+def quantize_pack_check(device=None, stream=None, workspace=None):
+    """Raise VarqError if a quantize+pack call that used `workspace` (default:
+    the cached workspace of the stream, itself defaulting to the current stream
+    of `device`) since the previous check ended a cross-work-group wait by its
+    time bound; synchronizes that stream."""
     dev = torch.device("cuda") if device is None else torch.device(device)
-    _check(lib().varq_quantize_pack_check(_stream(stream, dev)))
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    if workspace is None:
+        workspace = _WS.get((dev.index, _stream_obj(stream, dev).cuda_stream, "qp"))
+    wp, _ = _ws_args(workspace)
+    _check(lib().varq_quantize_pack_check(wp, _stream(stream, dev)))
 
 
 def frame_group_offsets(L, group_tokens, phase=0):
@@ -226,7 +301,7 @@ def grouped_scale_count(mode, B, L, H, D, G):
     return lib().varq_grouped_scale_count(GROUPINGS[mode], B, L, H, D, G)
 
 
-def quantize_pack_grouped(x, group_offsets, bits, mode, packed, scales, stream=None):
+def quantize_pack_grouped(x, group_offsets, bits, mode, packed, scales, stream=None, workspace=None):
     """x bf16 [B, L, H, D] -> rows [0, L) of `packed` [B, H, W, L_cap] and the
     compact scales of grouping `mode` (a contiguous fp32 tensor of at least
     grouped_scale_count(...) elements)."""
@@ -239,14 +314,25 @@ def quantize_pack_grouped(x, group_offsets, bits, mode, packed, scales, stream=N
         raise ValueError("packed and scales must be contiguous")
     B, L, H, D = x.shape
     off, G = _offsets(group_offsets)
+    if workspace is None and mode in ("channel_block", "channel"):
+        table = list(group_offsets) if mode == "channel_block" else [0, L]
+        workspace = get_workspace("qp", quantize_pack_workspace_bytes(B, H, D, table, bits, 1),
+                                           x.device, stream)
+    wp, wb = _ws_args(workspace)
     _check(lib().varq_quantize_pack_grouped(
         x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, H, D, L, GROUPINGS[mode], off, G, bits,
-        packed.data_ptr(), packed.shape[3], scales.data_ptr(), scales.numel(), _stream(stream, x.device)))
+        packed.data_ptr(), packed.shape[3], scales.data_ptr(), scales.numel(), wp, wb, _stream(stream, x.device)))
     return packed, scales
 
 
+def _attn_ws(workspace, B, H, D, Lq, L_kv, device, stream):
+    if workspace is None:
+        workspace = get_workspace("attn", attention_workspace_bytes(B, H, D, Lq, L_kv), device, stream)
+    return _ws_args(workspace)
+
+
 def packed_attention(q, packed_k, scales_k, packed_v, scales_v, group_offsets, bits,
-                     softmax_scale=None, out=None, stream=None):
+                     softmax_scale=None, out=None, stream=None, workspace=None):
     """q bf16 [B, Lq, H, D] attends to cache tokens [0, group_offsets[-1]) ->
     out bf16 [B, Lq, H, D]."""
     _need(q, torch.bfloat16, "q")
@@ -272,11 +358,12 @@ def packed_attention(q, packed_k, scales_k, packed_v, scales_v, group_offsets, b
         raise ValueError("out must have channel stride 1")
     off, G = _offsets(group_offsets)
     L_kv = int(group_offsets[-1])
+    wp, wb = _attn_ws(workspace, B, H, D, Lq, L_kv, q.device, stream)
     _check(lib().varq_packed_attention(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), B, H, D, Lq,
         packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
         packed_k.shape[3], scales_k.shape[2], L_kv, off, G, bits, softmax_scale,
-        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2), _stream(stream, q.device)))
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2), wp, wb, _stream(stream, q.device)))
     return out
 
 
@@ -288,7 +375,7 @@ def _rope_tables(rope_cos, rope_sin, rows, D):
 
 
 def packed_attention_rope(q, packed_k, scales_k, packed_v, scales_v, group_offsets, bits, rope_cos, rope_sin,
-                          softmax_scale=None, out=None, stream=None):
+                          softmax_scale=None, out=None, stream=None, workspace=None):
     """packed_attention over a cache whose K was quantized before RoPE: each
     dequantized K row t is rotated by rope_cos/rope_sin[t] (fp32 [>= L_kv, D/2])
     before the scores; q is already rotated."""
@@ -316,12 +403,13 @@ def packed_attention_rope(q, packed_k, scales_k, packed_v, scales_v, group_offse
     if out.stride(3) != 1:
         raise ValueError("out must have channel stride 1")
     off, G = _offsets(group_offsets)
+    wp, wb = _attn_ws(workspace, B, H, D, Lq, L_kv, q.device, stream)
     _check(lib().varq_packed_attention_rope(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), B, H, D, Lq,
         packed_k.data_ptr(), scales_k.data_ptr(), packed_v.data_ptr(), scales_v.data_ptr(),
         packed_k.shape[3], scales_k.shape[2], L_kv, off, G, bits, softmax_scale,
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
-        rope_cos.data_ptr(), rope_sin.data_ptr(), _stream(stream, q.device)))
+        rope_cos.data_ptr(), rope_sin.data_ptr(), wp, wb, _stream(stream, q.device)))
     return out
 
 
@@ -349,7 +437,7 @@ def unpack_dequant_rope(packed, scales, group_offsets, bits, rope_cos, rope_sin,
     return out
 
 
-def bf16_attention(q, k, v, L_kv=None, softmax_scale=None, out=None, stream=None):
+def bf16_attention(q, k, v, L_kv=None, softmax_scale=None, out=None, stream=None, workspace=None):
     """Unfused baseline: q bf16 [B, Lq, H, D] attends to dense bf16 k, v
     [B, H, L_rows, D] (e.g. unpack_dequant's output) over rows [0, L_kv) ->
     out bf16 [B, Lq, H, D]."""
@@ -370,10 +458,11 @@ def bf16_attention(q, k, v, L_kv=None, softmax_scale=None, out=None, stream=None
     _need(out, torch.bfloat16, "out")
     if out.stride(3) != 1:
         raise ValueError("out must have channel stride 1")
+    wp, wb = _attn_ws(workspace, B, H, D, Lq, L_kv, q.device, stream)
     _check(lib().varq_bf16_attention(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), B, H, D, Lq,
         k.data_ptr(), v.data_ptr(), L_rows, L_kv, softmax_scale,
-        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2), _stream(stream, q.device)))
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2), wp, wb, _stream(stream, q.device)))
     return out
 
 

@@ -75,7 +75,8 @@ def _qp(V, **kw):
     G = kw.get("G", len(a["off"]) - 1 if a["off"] is not None else 1)
     return V.lib().varq_quantize_pack(a["x"], a["sx_b"], a["sx_l"], a["sx_h"], a["B"], a["H"], a["D"],
                                       a["L_in"], off, G, a["bits"], a["packed"], a["L_cap"],
-                                      a["tok_start"], a["scales"], a["G_cap"], a["group_start"], None)
+                                      a["tok_start"], a["scales"], a["G_cap"], a["group_start"],
+                                      a.get("ws"), a.get("ws_bytes", 0), None)
 
 
 def test_quantize_pack_validation(V):
@@ -104,13 +105,14 @@ def _qpkv(V, **kw):
     """Call varq_quantize_pack_kv with defaults overridden by kw; returns the status."""
     a = dict(k=0x10000, sk_b=680 * 16 * 64, sk_l=16 * 64, sk_h=64, v=0x70000, sv_b=680 * 16 * 64, sv_l=16 * 64,
              sv_h=64, B=1, H=16, D=64, L_in=680, off=[0, 1, 5, 680], bits=4, packed_k=0x20000, scales_k=0x30000,
-             packed_v=0x40000, scales_v=0x50000, L_cap=680, tok_start=0, G_cap=3, group_start=0)
+             packed_v=0x40000, scales_v=0x50000, L_cap=680, tok_start=0, G_cap=3, group_start=0, ws=None,
+             ws_bytes=0)
     a.update(kw)
     off = (ctypes.c_int32 * len(a["off"]))(*a["off"])
     return V.lib().varq_quantize_pack_kv(
         a["k"], a["sk_b"], a["sk_l"], a["sk_h"], a["v"], a["sv_b"], a["sv_l"], a["sv_h"], a["B"], a["H"], a["D"],
         a["L_in"], off, len(a["off"]) - 1, a["bits"], a["packed_k"], a["scales_k"], a["packed_v"], a["scales_v"],
-        a["L_cap"], a["tok_start"], a["G_cap"], a["group_start"], None)
+        a["L_cap"], a["tok_start"], a["G_cap"], a["group_start"], a["ws"], a["ws_bytes"], None)
 
 
 def test_quantize_pack_kv_validation(V):
@@ -139,7 +141,48 @@ def _attn(V, **kw):
     return V.lib().varq_packed_attention(
         a["q"], a["sq_b"], a["sq_l"], a["sq_h"], a["B"], a["H"], a["D"], a["Lq"], a["pk"], a["sk"],
         a["pv"], a["sv"], a["L_cap"], a["G_cap"], a["L_kv"], off, G, a["bits"], a["scale"],
-        a["out"], a["so_b"], a["so_l"], a["so_h"], None)
+        a["out"], a["so_b"], a["so_l"], a["so_h"], None, 0, None)
+
+
+def _qp_ws(V, B, H, D, off, bits=4, n=1):
+    out = ctypes.c_int64(-1)
+    arr = (ctypes.c_int32 * len(off))(*off)
+    r = V.lib().varq_quantize_pack_workspace(B, H, D, off[-1], arr, len(off) - 1, bits, n, ctypes.byref(out))
+    return r, out.value
+
+
+def test_quantize_pack_workspace_query(V):
+    """Workspace = 16 bytes of launch state + 8 bytes per (unit, channel) and per
+    (block, channel), counting every tensor, and only when a block spans
+    several 16384-element units; a split call without enough workspace is
+    rejected before any launch."""
+    from synth import WORKLOADS
+    var = WORKLOADS["var_d30"]
+    assert _qp_ws(V, var.B, var.H, var.D, list(var.offsets)) == (0, 0)      # every block fits one unit
+    # one block of 300 rows at D = 128 (128-row units): 3 chunks per (b, h)
+    r1, n1 = _qp_ws(V, 2, 3, 128, [0, 300])
+    assert r1 == 0 and n1 == 16 + (2 * 3 * 3 + 2 * 3 * 1) * 128 * 8
+    r2, n2 = _qp_ws(V, 2, 3, 128, [0, 300], n=2)
+    assert r2 == 0 and n2 == 16 + 2 * (2 * 3 * 3 + 2 * 3 * 1) * 128 * 8
+    # a 4-row block packed with the 300-row block's chunks: 1 + 3 units
+    assert _qp_ws(V, 1, 1, 128, [0, 4, 304])[1] == 16 + (4 + 2) * 128 * 8
+    assert _qp_ws(V, 1, 1, 128, [0, 4, 304], bits=9)[0] == -2
+    assert _qp_ws(V, 1, 1, 128, [0, 4, 304], n=3)[0] == -1
+    assert _qp_ws(V, 1, 1, 128, [0, 4, 4])[0] == -1
+    sf = WORKLOADS["self_forcing"]
+    r, n = _qp_ws(V, sf.B, sf.H, sf.D, [0, 1560, 3120, 4680], n=2)
+    assert r == 0 and n == 16 + 2 * sf.B * sf.H * (3 * 13 + 3) * 128 * 8
+    # the split call itself: NULL or too small a workspace is VARQ_EWORKSPACE
+    kw = dict(x=0x10000, sx_b=300 * 3 * 128, sx_l=3 * 128, sx_h=128, B=2, H=3, D=128, L_in=300, off=[0, 300],
+              packed=0x20000, L_cap=304, scales=0x30000, G_cap=1)
+    assert _qp(V, **kw) == -7 and "workspace" in V.last_error()
+    assert _qp(V, ws=0x40000, ws_bytes=n1 - 8, **kw) == -7
+    assert _qp(V, ws=0x40008, ws_bytes=n1, **kw) == -3           # not 16-byte aligned
+    kv = dict(k=0x10000, sk_b=300 * 3 * 128, sk_l=3 * 128, sk_h=128, v=0x70000, sv_b=300 * 3 * 128,
+              sv_l=3 * 128, sv_h=128, B=2, H=3, D=128, L_in=300, off=[0, 300], L_cap=304, G_cap=1)
+    assert _qpkv(V, ws=0x40000, ws_bytes=n1, **kv) == -7         # one tensor's worth is too small for two
+    # the check accepts a NULL workspace (nothing to report)
+    assert V.lib().varq_quantize_pack_check(None, None) == 0
 
 
 def test_packed_attention_validation(V):
@@ -162,7 +205,8 @@ def test_bf16_attention_validation(V):
 
     def call(D=64, Lq=16, q=0x10000, k=0x20000, v=0x30000, L_rows=64, L_kv=64, scale=0.125, out=0x40000,
              sq=(64 * 16 * 64, 16 * 64, 64), so=(64 * 16 * 64, 16 * 64, 64)):
-        return f(q, sq[0], sq[1], sq[2], 1, 16, D, Lq, k, v, L_rows, L_kv, scale, out, so[0], so[1], so[2], None)
+        return f(q, sq[0], sq[1], sq[2], 1, 16, D, Lq, k, v, L_rows, L_kv, scale, out, so[0], so[1], so[2],
+                 None, 0, None)
 
     assert call(D=96) == -6
     assert call(Lq=0) == 0
@@ -192,7 +236,24 @@ def selftest():
                                                    ctypes.POINTER(ctypes.c_longlong)]
     lib.varq_selftest_dequant.restype = ctypes.c_longlong
     lib.varq_selftest_dequant.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32]
+    lib.varq_selftest_attn_max_token.restype = ctypes.c_longlong
+    lib.varq_selftest_attn_max_token.argtypes = [ctypes.c_int]
     return lib
+
+
+def test_attention_tile_loads_stay_in_cache(selftest):
+    """The packed attention's 16-byte tile loads (4 tokens of one word plane)
+    never read past the smallest cache the library accepts for the window,
+    L_cap = L_kv rounded up to a multiple of 8, for every window length modulo
+    the 64-token tile and for every workload's windows; every token of the
+    window is still loaded."""
+    from synth import WORKLOADS
+    lens = list(range(1, 1025)) + [w.offsets[-1] for w in WORKLOADS.values()]
+    lens += [c[2] for w in WORKLOADS.values() for c in w.calls] + [4680 * j + r for j in range(1, 8) for r in (1, 7, 63)]
+    for L in lens:
+        hi = selftest.varq_selftest_attn_max_token(L)
+        assert hi >= 0, (L, hi)                          # -2 would mean a misaligned item
+        assert L - 1 <= hi < (L + 7) // 8 * 8, (L, hi)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
@@ -220,7 +281,7 @@ def _qpg(V, **kw):
     off = (ctypes.c_int32 * len(a["off"]))(*a["off"])
     return V.lib().varq_quantize_pack_grouped(a["x"], a["sx_b"], a["sx_l"], a["sx_h"], a["B"], a["H"], a["D"],
                                               a["L"], a["mode"], off, len(a["off"]) - 1, a["bits"], a["packed"],
-                                              a["L_cap"], a["scales"], a["n_scales"], None)
+                                              a["L_cap"], a["scales"], a["n_scales"], None, 0, None)
 
 
 def test_grouped_scale_count_matches_oracle(V):
@@ -276,5 +337,5 @@ def test_rope_entry_validation(V):
     pa = V.lib().varq_packed_attention_rope
     args = [0x10000, 256 * 16 * 64, 16 * 64, 64, 1, 16, 64, 256, 0x20000, 0x30000, 0x40000, 0x50000,
             680, 2, 680, off, 2, 4, 0.125, 0x60000, 256 * 16 * 64, 16 * 64, 64]
-    assert pa(*args, 0x70000, None, None) == -1
-    assert pa(*args, 0x70001, 0x80000, None) == -3
+    assert pa(*args, 0x70000, None, None, 0, None) == -1
+    assert pa(*args, 0x70001, 0x80000, None, 0, None) == -3
