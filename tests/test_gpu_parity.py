@@ -181,14 +181,15 @@ def _sampled_qp(V, wl, bits, pairs):
             w, s = O.quantize_pack(xs, off, bits)
             assert np.array_equal(_words(pk[b:b + 1, h:h + 1], wl.L), w), (name, b, h)
             assert np.array_equal(_f32bits(sk[b:b + 1, h:h + 1]), s.view(np.uint32)), (name, b, h)
-        # properties at full size: codes in range, each (b, h, block, channel)
-        # group reaches +-qmax unless the whole group is zero
-        q = torch.from_numpy(O.unpack_words(_words(pk[:1], wl.L), wl.D, bits))
+        # properties at full size, every batch element: codes in range, each
+        # (b, h, block, channel) group reaches +-qmax (no group is all zero)
         qm = O.qmax(bits)
-        assert int(q.abs().max()) <= qm
-        for g in range(wl.G):
-            amax = q[:, :, off[g]:off[g + 1], :].abs().amax(dim=2)
-            assert bool((amax == qm).all())
+        for b in range(wl.B):
+            q = torch.from_numpy(O.unpack_words(_words(pk[b:b + 1], wl.L), wl.D, bits))
+            assert int(q.abs().max()) <= qm
+            for g in range(wl.G):
+                amax = q[:, :, off[g]:off[g + 1], :].abs().amax(dim=2)
+                assert bool((amax == qm).all()), (name, b, g)
         del pk, sk
 
 
@@ -197,10 +198,7 @@ def _sampled_qp(V, wl, bits, pairs):
 def test_quantize_pack_large_sampled(V, name, bits):
     wl = WORKLOADS[name]
     _say(f"[qp {name} bits={bits}]")
-    rng = np.random.default_rng(11)
-    pairs = [(0, 0), (wl.B - 1, wl.H - 1)] + [(int(rng.integers(wl.B)), int(rng.integers(wl.H)))
-                                              for _ in range(2)]
-    _sampled_qp(V, wl, bits, pairs)
+    _sampled_qp(V, wl, bits, _sample_pairs(wl, 11))
 
 
 def test_incremental_append_equals_one_shot(V):
@@ -306,6 +304,8 @@ def _assert_attn(got, ob, C, literal=False, tag=""):
                "frac_C<=2": float(small.mean())}
         _say(f"  {tag} literal {lit}")
         assert lit["max_abs_C<=2"] <= MAXE and lit["mean_abs_C<=2"] <= MEANE, lit
+        # the literal rule must cover most of the output, or it proves little
+        assert lit["frac_C<=2"] >= 0.25, lit
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
@@ -481,15 +481,21 @@ def test_attention_var_d30_full(V, bits):
         _assert_attn(_gpu_rows(out), ob, C, literal=unit_v, tag=f"unit_v={unit_v}")
 
 
+def _sample_pairs(wl, seed):
+    """Two fixed (batch, head) pairs (first and last) and four seeded ones."""
+    rng = np.random.default_rng(seed)
+    return [(0, 0), (wl.B - 1, wl.H - 1)] + [(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(4)]
+
+
 @pytest.mark.parametrize("name,bits", [("infinity_8b", 4), ("infinity_8b", 2), ("self_forcing", 4),
                                        ("longlive", 3), ("longlive", 2)])
 def test_attention_large_sampled(V, name, bits):
-    """Full-size launch; the oracle checks sampled (batch, head) pairs."""
+    """Full-size launch; the oracle checks two fixed and four seeded (batch,
+    head) pairs (seed 5), all queries of each."""
     wl = WORKLOADS[name]
-    _say(f"[attn {name} bits={bits}]")
     off = list(wl.offsets)
-    rng = np.random.default_rng(5)
-    pairs = [(0, 0), (wl.B - 1, wl.H - 1), (int(rng.integers(wl.B)), int(rng.integers(wl.H)))]
+    pairs = _sample_pairs(wl, 5)
+    _say(f"[attn {name} bits={bits}] pairs {pairs}")
     for unit_v in (False, True):
         k, v, q = workload_inputs(wl, seed=0, device=DEV, unit_v=unit_v)
         out, _ = _gpu_attention(V, k, v, q, off, bits)
