@@ -19,6 +19,8 @@
  *    work-group, the partial results of attention launches split over KV
  *    ranges) take a caller-owned `workspace` of at least the bytes that the
  *    matching *_workspace query returns (NULL is accepted when it returns 0).
+ *    Only varq_quantize_pack_kv_noalloc, for callers that cannot allocate,
+ *    uses a fixed device array inside the library instead.
  *  - `group_offsets` is a HOST array of G+1 int32 prefix offsets
  *    0 = o_0 < o_1 < ... < o_G: block g covers tokens [o_g, o_{g+1}).
  *    G <= VARQ_MAX_GROUPS per call.
@@ -156,6 +158,30 @@ int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_
                           int32_t *packed_k, float *scales_k, int32_t *packed_v, float *scales_v,
                           int64_t L_cap, int64_t tok_start, int64_t G_cap, int64_t group_start,
                           void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * varq_quantize_pack_kv for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without a workspace and the same outputs,
+ * bit for bit. The cross-work-group exchange uses a fixed 16 MiB array inside
+ * the library instead, one per device, kept until the process ends; the call
+ * itself allocates nothing. A call whose exchange would need more than 16 MiB
+ * (16 bytes + 8 bytes per (chunk, channel) and per (block, channel) of both
+ * tensors, as varq_quantize_pack_workspace with n_tensors = 2 counts it)
+ * returns VARQ_EWORKSPACE and launches nothing. The first call on a device
+ * that needs the array enqueues a kernel zeroing it on `stream` before its own
+ * launch. Every call on one device shares that device's array and leaves it
+ * valid for the next, so calls that may overlap on one device (other streams,
+ * other threads) race: order them on one stream. varq_quantize_pack_check
+ * with a NULL workspace reports this array's status on the current device.
+ */
+int varq_quantize_pack_kv_noalloc(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_h,
+                                  const void *v, int64_t sv_b, int64_t sv_l, int64_t sv_h,
+                                  int B, int H, int D, int64_t L_in,
+                                  const int32_t *group_offsets, int G_in, int bits,
+                                  int32_t *packed_k, float *scales_k, int32_t *packed_v, float *scales_v,
+                                  int64_t L_cap, int64_t tok_start, int64_t G_cap, int64_t group_start,
+                                  void *stream);
 
 /*
  * Pre-RoPE quantization (project page Appendix F / Table 7; Insight 03, Eq. 3):
@@ -349,7 +375,9 @@ int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
  * wait cut short leaves that call's outputs invalid. Synchronizes `stream` (a
  * hipStream_t; NULL = the null stream; the stream the calls ran on) and reads
  * the status word in the workspace's launch state.
- * Returns VARQ_OK (also for a NULL workspace or one no such launch used), or
+ * A NULL workspace means the fixed array of varq_quantize_pack_kv_noalloc on
+ * the current device.
+ * Returns VARQ_OK (also when no such launch used the workspace or array), or
  * VARQ_ELAUNCH after a timed-out wait (the status is then cleared) or when the
  * status cannot be read. */
 int varq_quantize_pack_check(void *workspace, void *stream);

@@ -97,6 +97,68 @@ int check_workspace(const void *ws, int64_t have, int64_t need, const char *what
     return VARQ_OK;
 }
 
+// Fixed exchange scratch of varq_quantize_pack_kv_noalloc (for callers that
+// cannot allocate): one array per device, held by the loaded library until
+// the process ends. In host code the array's name is no device address; the
+// address comes from hipGetSymbolAddress, looked up once per device with that
+// device current, and only that pointer is passed to kernels.
+constexpr int64_t kNoallocScratchBytes = int64_t(16) << 20;
+constexpr int kNoallocMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+__global__ void clear_scratch(uint4 *p, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct NoallocScratch {
+    void *ptr = nullptr;    // device address of `scratch` on this device
+    bool cleared = false;   // the clearing kernel has been enqueued
+};
+std::mutex g_noalloc_mu;
+NoallocScratch g_noalloc[kNoallocMaxDevices];
+
+// This device's fixed scratch. On the first use on a device the address is
+// looked up and a kernel that zeroes the whole array (the launch state and
+// every tagged slot must start at zero) is enqueued on `st`, ahead of the
+// call's own launch.
+int noalloc_scratch(hipStream_t st, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VARQ_ELAUNCH, "quantize_pack_kv_noalloc: no current device");
+    if (dev < 0 || dev >= kNoallocMaxDevices)
+        return fail(VARQ_EUNSUPPORTED, "quantize_pack_kv_noalloc: device ordinal %d beyond %d", dev,
+                    kNoallocMaxDevices - 1);
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    NoallocScratch &s = g_noalloc[dev];
+    if (!s.ptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(VARQ_ELAUNCH, "quantize_pack_kv_noalloc: hipGetSymbolAddress failed: HIP error %d (%s)",
+                        (int)e, hipGetErrorString(e));
+        s.ptr = p;
+    }
+    if (!s.cleared) {
+        hipLaunchKernelGGL(clear_scratch, dim3(1024), dim3(256), 0, st, static_cast<uint4 *>(s.ptr),
+                           kNoallocScratchBytes / 16);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(VARQ_ELAUNCH, "quantize_pack_kv_noalloc: clearing the scratch failed: HIP error %d (%s)",
+                        (int)e, hipGetErrorString(e));
+        s.cleared = true;
+    }
+    *out = s.ptr;
+    return VARQ_OK;
+}
+
+// This device's fixed scratch if a no-allocation call has set it up, else NULL.
+void *noalloc_scratch_if_set() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    return g_noalloc[dev].cleared ? g_noalloc[dev].ptr : nullptr;
+}
+
 int device_cus() {
     static std::mutex mu;
     static std::map<int, int> cus;
@@ -415,6 +477,43 @@ int varq_quantize_pack_kv(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_
     return qp_launch(a, bits, split, max_nc, workspace, workspace_bytes, stream);
 }
 
+int varq_quantize_pack_kv_noalloc(const void *k, int64_t sk_b, int64_t sk_l, int64_t sk_h,
+                                  const void *v, int64_t sv_b, int64_t sv_l, int64_t sv_h,
+                                  int B, int H, int D, int64_t L_in,
+                                  const int32_t *group_offsets, int G_in, int bits,
+                                  int32_t *packed_k, float *scales_k, int32_t *packed_v, float *scales_v,
+                                  int64_t L_cap, int64_t tok_start, int64_t G_cap, int64_t group_start,
+                                  void *stream) {
+    varq::QuantPackArgs a, av;
+    bool empty = false, split = false;
+    int max_nc = 1;
+    if (int r = qp_setup(k, sk_b, sk_l, sk_h, B, H, D, L_in, group_offsets, G_in, bits, packed_k, L_cap, tok_start,
+                         scales_k, G_cap, group_start, a, &empty, &split, &max_nc))
+        return r;
+    if (int r = qp_setup(v, sv_b, sv_l, sv_h, B, H, D, L_in, group_offsets, G_in, bits, packed_v, L_cap, tok_start,
+                         scales_v, G_cap, group_start, av, &empty, &split, &max_nc))
+        return r;
+    if (empty) return ok();
+    if (packed_k == packed_v || scales_k == scales_v)
+        return fail(VARQ_EINVAL, "quantize_pack_kv_noalloc: K and V need caches of their own");
+    a.x2 = av.x;
+    a.sx2_b = av.sx_b; a.sx2_l = av.sx_l; a.sx2_h = av.sx_h;
+    a.packed2 = av.packed;
+    a.scales2 = av.scales;
+    a.n_units = 2 * a.n_units_one;
+    void *ws = nullptr;
+    if (split) {
+        const int64_t need = qp_workspace_bytes(a.n_units, (int64_t)2 * B * H * G_in, D);
+        if (need > kNoallocScratchBytes)
+            return fail(VARQ_EWORKSPACE,
+                        "quantize_pack_kv_noalloc: this call needs %lld bytes of exchange scratch, more than the "
+                        "fixed %lld bytes; use varq_quantize_pack_kv with a workspace",
+                        (long long)need, (long long)kNoallocScratchBytes);
+        if (int r = noalloc_scratch(static_cast<hipStream_t>(stream), &ws)) return r;
+    }
+    return qp_launch(a, bits, split, max_nc, ws, kNoallocScratchBytes, stream);
+}
+
 int64_t varq_grouped_scale_count(int mode, int B, int64_t L, int H, int D, int G) {
     if (B < 0 || L < 0 || H < 0 || D < 0 || G < 0) return -1;
     switch (mode) {
@@ -697,6 +796,7 @@ int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
 }
 
 int varq_quantize_pack_check(void *workspace, void *stream) {
+    if (!workspace) workspace = noalloc_scratch_if_set();
     if (!workspace) return ok();
     const hipStream_t st = static_cast<hipStream_t>(stream);
     uint32_t *status_word = static_cast<uint32_t *>(workspace) + 2;     // launch state {epoch, finished, status}
