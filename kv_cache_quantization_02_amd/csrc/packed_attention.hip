@@ -38,7 +38,14 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int AT_NT = 64;        // KV tokens per tile
-constexpr int AT_SL_MAXG = 32;   // blocks whose K and V scales a work-group can hold in LDS
+// LDS operand reads run this many matrix steps ahead of their use in the
+// interleaved phases of a tile
+constexpr int AT_RA = 2;
+// blocks whose K and V scales a work-group holds in LDS: at head_dim 64 two
+// work-groups still share a CU's LDS, at 128 (one work-group per CU) the
+// scales of 64 blocks take 64 KB next to the 72 KB of tile buffers
+template <int D>
+constexpr int at_sl_maxg() { return D == 64 ? 32 : 64; }
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -76,9 +83,14 @@ struct AttnTile {
     static constexpr int THREADS = 64 * NW;
     static constexpr int QW = 32 * QB;        // queries per wave
     static constexpr int QT = NW * QW;        // queries per work-group
-    static constexpr int NITEMS = 32 * W;     // 16W K items then 16W V items (4 tokens each)
+    // 16W K items (4 tokens of one word plane each), then 16W V items. The K
+    // items' slots are padded to whole waves, so every wave holds items of one
+    // kind (or none) at each of its IPT positions.
+    static constexpr int NK = 16 * W;
+    static constexpr int NKP = (NK + 63) / 64 * 64;
+    static constexpr int NSLOTS = NKP + NK;
     static constexpr int WORDS = DENSE ? 16 : 4;   // 32-bit words an item loads
-    static constexpr int IPT = (NITEMS + THREADS - 1) / THREADS;
+    static constexpr int IPT = (NSLOTS + THREADS - 1) / THREADS;
 };
 
 // V^T tile in LDS: row = channel; inside each 16-token group the four 4-token
@@ -89,7 +101,7 @@ __device__ inline int v_pos(int tok) {
     return (tok & ~15) + 4 * (((q & 1) << 1) | (q >> 1)) + (tok & 3);
 }
 
-// SL: the (batch, head)'s K and V scales (at most AT_SL_MAXG blocks) are
+// SL: the (batch, head)'s K and V scales (at most at_sl_maxg<D>() blocks) are
 // copied to LDS once, and dequantization reads them there; otherwise each
 // tile's scales are prefetched from memory with its words.
 // ROPE (pre-RoPE quantization, project page Appendix F / Table 7): K was
@@ -102,7 +114,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     constexpr bool DENSE = T::DENSE;
     constexpr int CPW = T::CPW, W = T::W, KP = T::KP, VP = T::VP;
     constexpr int THREADS = T::THREADS, QW = T::QW, QT = T::QT;
-    constexpr int NITEMS = T::NITEMS, IPT = T::IPT;
+    constexpr int NKP = T::NKP, NSLOTS = T::NSLOTS, IPT = T::IPT;
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
     constexpr int KBUF = AT_NT * KP, VBUF = D * VP;
@@ -110,7 +122,8 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
     __shared__ int32_t off[VARQ_MAX_GROUPS_DEV + 1];
-    __shared__ __attribute__((aligned(16))) float sS[SL ? 2 * AT_SL_MAXG * D : 4];   // K rows, then V rows
+    constexpr int SLG = at_sl_maxg<D>();
+    __shared__ __attribute__((aligned(16))) float sS[SL ? 2 * SLG * D : 4];   // K rows, then V rows
 
     const int n_blocks = a.n_qtiles * a.B * a.H * a.kv_splits;
     const int lid = (int)xcd_logical_id(blockIdx.x, n_blocks);
@@ -127,16 +140,38 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     const int lr = lane & 31, hf = lane >> 5;
 
     for (int i = tid; i <= a.G; i += THREADS) off[i] = a.off[i];
-    // scales kept in LDS: one float4 of K and one of V per thread at most
-    // (AT_SL_MAXG * D / 4 <= THREADS), loaded now and stored once the loads
-    // below have all been waited for
-    static_assert(!SL || AT_SL_MAXG * D / 4 <= THREADS, "one scale vector per thread");
-    const bool sl_mine = SL && tid < a.G * (D / 4);
+    // scales kept in LDS: up to SLP float4 of K and as many of V per thread.
+    // With one of each they are loaded now and stored once the loads below
+    // have all been waited for; with more they are copied first, before any
+    // other load is in flight, so that no register holds them for long.
+    constexpr int SLP = SL ? (SLG * D / 4 + THREADS - 1) / THREADS : 1;
     float4 sl_k = make_float4(0.f, 0.f, 0.f, 0.f), sl_v = sl_k;
     if constexpr (SL) {
-        if (sl_mine) {
-            sl_k = reinterpret_cast<const float4 *>(a.sk + (int64_t)bh * a.G_cap * D)[tid];
-            sl_v = reinterpret_cast<const float4 *>(a.sv + (int64_t)bh * a.G_cap * D)[tid];
+        const float4 *gk = reinterpret_cast<const float4 *>(a.sk + (int64_t)bh * a.G_cap * D);
+        const float4 *gv = reinterpret_cast<const float4 *>(a.sv + (int64_t)bh * a.G_cap * D);
+        if constexpr (SLP == 1) {
+            if (tid < a.G * (D / 4)) {
+                sl_k = gk[tid];
+                sl_v = gv[tid];
+            }
+        } else {
+            // loads past the scales re-read the last vector (not stored)
+            const int n4 = a.G * (D / 4);
+            float4 ck[SLP], cv[SLP];
+#pragma unroll
+            for (int i = 0; i < SLP; ++i) {
+                const int e = min(tid + THREADS * i, n4 - 1);
+                ck[i] = gk[e];
+                cv[i] = gv[e];
+            }
+#pragma unroll
+            for (int i = 0; i < SLP; ++i) {
+                const int e = tid + THREADS * i;
+                if (e < n4) {
+                    reinterpret_cast<float4 *>(sS)[e] = ck[i];
+                    reinterpret_cast<float4 *>(sS + SLG * D)[e] = cv[i];
+                }
+            }
         }
     }
 
@@ -147,7 +182,9 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     const int n_begin = t_begin * AT_NT, g_begin = a.split_g0[split];
 
     // ---------------- items of 4 tokens: K items plane-fastest, V items
-    // token-fastest, which makes both LDS write patterns bank-conflict free
+    // token-fastest, which makes both LDS write patterns bank-conflict free.
+    // Slot it < NKP is K item it, slot NKP + j is V item j: the kind of an
+    // item is the same across a wave.
     const uint32_t *plane[IPT];
     const float *sbase[IPT];
     int it_w[IPT], it_t4[IPT];
@@ -155,13 +192,13 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
 #pragma unroll
     for (int r = 0; r < IPT; ++r) {
         const int it = tid + THREADS * r;
-        it_ok[r] = it < NITEMS;
-        const bool isV = it >= 16 * W;
-        const int j = isV ? it - 16 * W : it;
+        const bool isV = __builtin_amdgcn_readfirstlane(it >= NKP ? 1 : 0) != 0;
+        const int j = isV ? it - NKP : it;
+        it_ok[r] = j < 16 * W && it < NSLOTS;
         it_v[r] = isV;
         it_w[r] = isV ? (j >> 4) : (j % W);
         it_t4[r] = isV ? (j & 15) : (j / W);
-        if (!it_ok[r]) { it_w[r] = 0; it_t4[r] = 0; it_v[r] = false; }
+        if (!it_ok[r]) { it_w[r] = 0; it_t4[r] = 0; }      // it_v stays the wave's kind
         if constexpr (DENSE)
             plane[r] = reinterpret_cast<const uint32_t *>((it_v[r] ? a.vd : a.kd) + (int64_t)bh * a.L_cap * D +
                                                           it_w[r] * CPW);
@@ -171,8 +208,9 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     }
 
     // Prefetched tile: words per item and, when the tile lies in one block and
-    // scales are not in LDS, that block's scales for the item's channels. Two
-    // sets alternate so that a tile's loads are issued two tiles ahead.
+    // scales are not in LDS, that block's scales for the item's channels. A
+    // tile's loads are issued right after the tile before it is staged, a
+    // whole tile's compute ahead of their use.
     struct Pref {
         uint32_t wd[IPT][T::WORDS];
         float sc[IPT][CPW];
@@ -267,9 +305,9 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     if constexpr (SL) {
-        if (sl_mine) {
+        if (SLP == 1 && tid < a.G * (D / 4)) {
             reinterpret_cast<float4 *>(sS)[tid] = sl_k;
-            reinterpret_cast<float4 *>(sS + AT_SL_MAXG * D)[tid] = sl_v;
+            reinterpret_cast<float4 *>(sS + SLG * D)[tid] = sl_v;
         }
     }
 
@@ -389,7 +427,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
             const int ncw = min(CPW, D - cbase);
             if constexpr (SL) {
                 // scale rows in LDS: one per token (the tile's block unless split)
-                const float *base = sS + (it_v[r] ? AT_SL_MAXG * D : 0) + cbase;
+                const float *base = sS + (it_v[r] ? SLG * D : 0) + cbase;
                 if (!P.split) {
                     float scl[CPW];
                     scale_row(scl, base + P.g * D, ncw);
@@ -453,7 +491,7 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     // the tile is issued as: scores of half 0; scores of half 1 interleaved
     // with the exponentials of half 0; P*V of half 0 interleaved with the
     // exponentials of half 1; P*V of half 1.
-    auto compute = [&](int buf, int n0, bool masked) {
+    auto compute = [&](int buf, int n0, bool masked) __attribute__((always_inline)) {
         if (wave_idle) return;
         const uint16_t *Kb = Ks + buf * KBUF + lr * KP + 8 * hf;
         const uint16_t *Vb = Vt + buf * VBUF + lr * VP + 8 * hf;
@@ -568,15 +606,16 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         {
             constexpr int NS = KSTEPS;                  // matrix steps (x QB ops each)
             constexpr int NJ = 8 * QB;                  // exponential pairs
-            bf16x8 kop[2];
-            kop[0] = kread(1, 0);
+            bf16x8 kop[AT_RA + 1];
+#pragma unroll
+            for (int i = 0; i < AT_RA && i < NS; ++i) kop[i] = kread(1, i);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < NS; ++k) {
-                if (k + 1 < NS) kop[(k + 1) & 1] = kread(1, k + 1);
+                if (k + AT_RA < NS) kop[(k + AT_RA) % (AT_RA + 1)] = kread(1, k + AT_RA);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    s[1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k & 1], qop[qb][k], s[1][qb], 0, 0, 0);
+                    s[1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k % (AT_RA + 1)], qop[qb][k], s[1][qb], 0, 0, 0);
                 exps_part(0, NJ * k / NS, NJ * (k + 1) / NS - NJ * k / NS);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -587,15 +626,16 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         {
             constexpr int NS = 2 * DBLK;
             constexpr int NJ = 8 * QB;
-            bf16x8 vop[2];
-            vop[0] = vread(0, 0);
+            bf16x8 vop[AT_RA + 1];
+#pragma unroll
+            for (int i = 0; i < AT_RA && i < NS; ++i) vop[i] = vread(0, i);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < NS; ++k) {
-                if (k + 1 < NS) vop[(k + 1) & 1] = vread(0, k + 1);
+                if (k + AT_RA < NS) vop[(k + AT_RA) % (AT_RA + 1)] = vread(0, k + AT_RA);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    o[qb][k >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[k & 1], pop[0][qb][k & 1], o[qb][k >> 1], 0, 0, 0);
+                    o[qb][k >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[k % (AT_RA + 1)], pop[0][qb][k & 1], o[qb][k >> 1], 0, 0, 0);
                 exps_part(1, NJ * k / NS, NJ * (k + 1) / NS - NJ * k / NS);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -640,8 +680,9 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
             rope_tile(cur, n0);
             lds_barrier();
         }
-        // the next tile's dequantization follows this tile's compute and
-        // overlaps its last matrix ops
+        // the next tile's staging follows this tile's compute and overlaps
+        // its last matrix ops (dequantization interleaved with the matrix ops
+        // of the exponential-free phases measured slower)
         compute(cur, n0, false);
         dequant(cur ^ 1, P0, n0 + AT_NT);
         if (jt + 2 < t_end) prefetch(P0, n0 + 2 * AT_NT);
@@ -753,10 +794,10 @@ static hipError_t launch_at(const AttnArgs &a, hipStream_t st) {
                            dim3(64 * AT_CFG_NW), 0, st, a);
         return hipGetLastError();
     }
-    // head_dim 64 keeps up to AT_SL_MAXG blocks' scales in LDS (LDS still
-    // fits two work-groups per CU); otherwise scales stream with the words
-    if (D == 64 && a.G <= AT_SL_MAXG)
-        hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW, D == 64>), dim3((unsigned)grid),
+    // up to at_sl_maxg<D>() blocks' scales live in LDS; otherwise scales
+    // stream with the words
+    if (a.G <= at_sl_maxg<D>())
+        hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW, true>), dim3((unsigned)grid),
                            dim3(64 * AT_CFG_NW), 0, st, a);
     else
         hipLaunchKernelGGL((packed_attention_v5<BITS, D, AT_CFG_QB, AT_CFG_NW, false>), dim3((unsigned)grid),
