@@ -108,11 +108,16 @@ int varq_cache_bytes(int B, int H, int head_dim, int64_t L_cap, int64_t G_cap, i
  * (tok_start+L_in > L_cap or group_start+G_in > G_cap), VARQ_EUNSUPPORTED (a
  * block of more 16384-element chunks than resident work-groups, or a token
  * stride or cache length beyond 32-bit byte offsets), VARQ_ELAUNCH.
- * Workspace: when some block is longer than one work-group's 16384 elements
- * (16384 / D token rows), its chunks exchange per-channel maxima through the
- * caller's workspace (varq_quantize_pack_workspace gives the size: 16 bytes of
- * launch state plus 8 bytes per (chunk, channel) and per (block, channel);
- * otherwise the size is 0 and workspace may be NULL). The workspace must be
+ * Long blocks: a block longer than one work-group's 16384 elements (16384 / D
+ * token rows) is handled whole by one work-group per 16- or 32-channel slab
+ * when the long blocks follow all the short ones, bits is 2, 4, 7 or 8, D is
+ * a multiple of 16, no block exceeds 8192 rows and the long blocks form at
+ * most 16 runs of consecutive blocks that take one work-group shape (each
+ * block takes the smallest that holds it); such calls need no workspace. Otherwise its chunks exchange per-channel
+ * maxima through the caller's workspace (varq_quantize_pack_workspace gives
+ * the size: 16 bytes of launch state plus 8 bytes per (chunk, channel) and per
+ * (block, channel); it is 0 when no exchange is needed, and workspace may then
+ * be NULL). The workspace must be
  * zero-filled once before its first use; every launch leaves it valid for the
  * next (each slot carries the tag of the launch that wrote it, and the launch
  * state advances the tag), so it is then reused without clearing, by calls of

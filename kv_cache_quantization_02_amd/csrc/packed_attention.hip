@@ -30,6 +30,9 @@
 #include "varq_device.h"
 #include "varq_tile_math.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace varq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -62,6 +65,52 @@ template <int BITS>
 __device__ inline float field_f32(uint32_t word, int i) {
     constexpr int SHIFT = 32 - BITS;
     return (float)((int32_t)(word << (SHIFT - i * BITS)) >> SHIFT);
+}
+
+// (float)(int8_t)(byte J of x): one SDWA conversion of a sign-extended byte
+template <int J>
+__device__ inline float sbyte_f32(uint32_t x) {
+    float r;
+    if constexpr (J == 0)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(x));
+    else if constexpr (J == 1)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(x));
+    else if constexpr (J == 2)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(x));
+    else
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(x));
+    return r;
+}
+
+// Byte decode of INT4 and INT8 words: field i of an INT8 word is byte i; the
+// fields 2j, 2j + 1 of an INT4 word are byte j of (w << 4) & 0xF0F0F0F0 and of
+// w & 0xF0F0F0F0, each the code times 16 as a signed byte. Codes (times 16)
+// then take the scale (over 16) from the LDS table: the product, and its one
+// rounding, equal fp32(q) * s wherever s / 16 is exact.
+template <int BITS>
+struct ByteWord {
+    static_assert(BITS == 4 || BITS == 8, "byte decode");
+    uint32_t lo, hi;
+    __device__ explicit ByteWord(uint32_t w) {
+        if constexpr (BITS == 4) { lo = (w << 4) & 0xF0F0F0F0u; hi = w & 0xF0F0F0F0u; }
+        else { lo = w; hi = 0; }
+    }
+    // field I as a float: 16 q (INT4) or q (INT8)
+    template <int I>
+    __device__ float field() const {
+        if constexpr (BITS == 4) return sbyte_f32<I / 2>((I & 1) ? hi : lo);
+        else return sbyte_f32<I>(lo);
+    }
+};
+
+template <typename F, int... I>
+__device__ inline void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>)
+template <int N, typename F>
+__device__ inline void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // o *= alpha on an accumulator tile
@@ -140,6 +189,14 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     const int lr = lane & 31, hf = lane >> 5;
 
     for (int i = tid; i <= a.G; i += THREADS) off[i] = a.off[i];
+    // INT4 with scales in LDS: when every scale over 16 is exact, the table
+    // holds s / 16 for the byte decode (ByteWord); otherwise s
+    bool byte16 = false;
+    auto div16_exact = [](float4 v) {
+        auto ok1 = [](float x) { return x == 0.0f || x >= 0x1p-122f; };
+        return ok1(v.x) && ok1(v.y) && ok1(v.z) && ok1(v.w);
+    };
+    auto over16 = [](float4 v) { return make_float4(v.x * 0.0625f, v.y * 0.0625f, v.z * 0.0625f, v.w * 0.0625f); };
     // scales kept in LDS: up to SLP float4 of K and as many of V per thread.
     // With one of each they are loaded now and stored once the loads below
     // have all been waited for; with more they are copied first, before any
@@ -164,12 +221,16 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
                 ck[i] = gk[e];
                 cv[i] = gv[e];
             }
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < SLP; ++i) ok = ok && div16_exact(ck[i]) && div16_exact(cv[i]);
+            byte16 = BITS == 4 && __syncthreads_and(ok ? 1 : 0) != 0;
 #pragma unroll
             for (int i = 0; i < SLP; ++i) {
                 const int e = tid + THREADS * i;
                 if (e < n4) {
-                    reinterpret_cast<float4 *>(sS)[e] = ck[i];
-                    reinterpret_cast<float4 *>(sS + SLG * D)[e] = cv[i];
+                    reinterpret_cast<float4 *>(sS)[e] = byte16 ? over16(ck[i]) : ck[i];
+                    reinterpret_cast<float4 *>(sS + SLG * D)[e] = byte16 ? over16(cv[i]) : cv[i];
                 }
             }
         }
@@ -305,9 +366,13 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     if constexpr (SL) {
-        if (SLP == 1 && tid < a.G * (D / 4)) {
-            reinterpret_cast<float4 *>(sS)[tid] = sl_k;
-            reinterpret_cast<float4 *>(sS + SLG * D)[tid] = sl_v;
+        if constexpr (SLP == 1) {
+            const bool mine = tid < a.G * (D / 4);
+            byte16 = BITS == 4 && __syncthreads_and(!mine || (div16_exact(sl_k) && div16_exact(sl_v)) ? 1 : 0) != 0;
+            if (mine) {
+                reinterpret_cast<float4 *>(sS)[tid] = byte16 ? over16(sl_k) : sl_k;
+                reinterpret_cast<float4 *>(sS + SLG * D)[tid] = byte16 ? over16(sl_v) : sl_v;
+            }
         }
     }
 
@@ -375,6 +440,40 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         }
     };
 
+    // item r by byte decode (INT8, or INT4 with s / 16 in the LDS table):
+    // the same values as dequant_item
+    auto dequant_item_bytes = [&](int buf, const Pref &P, int r, const float (&sc)[CPW]) {
+        if constexpr (BITS == 4 || BITS == 8) {
+            uint16_t *K = Ks + buf * KBUF;
+            uint16_t *V = Vt + buf * VBUF;
+            const int cbase = it_w[r] * CPW, t4 = it_t4[r];
+            if (it_v[r]) {
+                const ByteWord<BITS> b0(P.wd[r][0]), b1(P.wd[r][1]), b2(P.wd[r][2]), b3(P.wd[r][3]);
+                const int p0 = v_pos(4 * t4);
+                static_for<CPW>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    const float sv = sc[i];
+                    const uint2 lo = make_uint2(pack_bf16x2(b0.template field<i>() * sv, b1.template field<i>() * sv),
+                                                pack_bf16x2(b2.template field<i>() * sv, b3.template field<i>() * sv));
+                    *reinterpret_cast<uint2 *>(V + (cbase + i) * VP + p0) = lo;
+                });
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const ByteWord<BITS> bw(P.wd[r][k]);
+                    uint32_t pw[CPW / 2];
+                    static_for<CPW / 2>([&](auto J) {
+                        constexpr int j = decltype(J)::value;
+                        pw[j] = pack_bf16x2(bw.template field<2 * j>() * sc[2 * j], bw.template field<2 * j + 1>() * sc[2 * j + 1]);
+                    });
+                    uint16_t *dst = K + (4 * t4 + k) * KP + cbase;
+                    if constexpr (CPW == 8) *reinterpret_cast<uint4 *>(dst) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+                    else *reinterpret_cast<uint2 *>(dst) = make_uint2(pw[0], pw[1]);
+                }
+            }
+        }
+    };
+
     // CPW scales of one block row from LDS (row = that block's D scales,
     // offset by the item's first channel): 16-byte reads when whole words
     // tile the row, the channel past the row's end clamped otherwise
@@ -431,7 +530,14 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
                 if (!P.split) {
                     float scl[CPW];
                     scale_row(scl, base + P.g * D, ncw);
-                    dequant_item(buf, P, r, [&](int, int i) { return scl[i]; });
+                    if constexpr (BITS == 8) {
+                        dequant_item_bytes(buf, P, r, scl);
+                    } else if constexpr (BITS == 4) {
+                        if (byte16) dequant_item_bytes(buf, P, r, scl);
+                        else dequant_item(buf, P, r, [&](int, int i) { return scl[i]; });
+                    } else {
+                        dequant_item(buf, P, r, [&](int, int i) { return scl[i]; });
+                    }
                 } else {
                     // a tile with a block boundary: each token takes the scale
                     // row of its own block; the same vector path for every item,
@@ -446,7 +552,9 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
                             g = group_of(off, g, min(t0 + k, L_kv - 1));
                             scale_row(scl[k], base + g * D, ncw);
                         }
-                        dequant_item(buf, P, r, [&](int k, int i) { return scl[k][i]; });
+                        // a table of s / 16 (exact) gives back s times 16
+                        const float tm = byte16 ? 16.0f : 1.0f;
+                        dequant_item(buf, P, r, [&](int k, int i) { return scl[k][i] * tm; });
                     } else {
                         // wider words: scales read where used, to bound registers
                         const float *row[4];

@@ -701,6 +701,197 @@ __global__ __launch_bounds__(QP_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
     }
 }
 
+// ---------------------------------------------------------------- slab kernel
+//
+// Blocks longer than one unit, without any exchange between work-groups: a
+// work-group owns one (tensor, batch, head, block) and SW consecutive channels
+// (a slab) for ALL the block's rows, so each channel's absmax is complete
+// inside it. Thread (r0, q) holds channels [8q, 8q + 8) of the slab in rows
+// r0, r0 + RS, ..., RPT rows (RS = NT / (SW / 8) rows per step, NT = 512 or
+// 1024 threads); all its row loads are issued at once, rows past the block
+// re-read its last row. The
+// maxima are reduced across the lanes of a wave that share q, then across
+// waves with LDS max-atomics; each channel's scale s = fp32(m / qmax) is
+// stored, and the codes (the same division-free exact quotient as the unit
+// kernel) are packed in registers: at 4 bits a lane's 8 channels are one
+// word, at 7 and 8 bits two, at 2 bits a lane pair's 16 channels one word.
+// Packing needs whole words inside a slab: BITS in {2, 4, 7, 8}.
+
+template <int BITS, int SW, int RPT, int NT>
+__global__ __launch_bounds__(NT) void quant_slab_kernel(const SlabArgs a) {
+    static_assert(BITS == 2 || BITS == 4 || BITS == 7 || BITS == 8, "whole words per slab");
+    static_assert(SW % 16 == 0, "slabs of 16 or 32 channels");
+    constexpr int LPR = SW / 8;                    // threads per row
+    constexpr int RS = NT / LPR;                   // rows per step
+    constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
+    __shared__ uint32_t sh_max[SW];
+    __shared__ __attribute__((aligned(16))) float sh_s[SW];
+    __shared__ __attribute__((aligned(16))) float sh_y[SW];
+    __shared__ uint32_t sh_slow;
+
+    const int64_t lid = xcd_logical_id(blockIdx.x, a.n_units);
+    if (lid < 0) return;
+    // logical id = (((t * B*H + bh) * nbig + j) * slabs + c), largest blocks
+    // (the last ones) first; the slabs of one block run side by side
+    const int c = (int)(lid % a.slabs);
+    int64_t v = lid / a.slabs;
+    const int jr = (int)(v % a.nbig);
+    v /= a.nbig;
+    const int bh = (int)(v % ((int64_t)a.B * a.H));
+    const int t = (int)(v / ((int64_t)a.B * a.H));
+    const int g = a.gb + (a.nbig - 1 - jr);
+    const int row0 = a.off[g], n = a.off[g + 1] - row0;
+    const int b = bh / a.H, h = bh % a.H;
+
+    const int tid = threadIdx.x;
+    const int q = tid % LPR, r0 = tid / LPR;
+    if (tid < SW) sh_max[tid] = 0;
+    if (tid == 0) sh_slow = 0;
+
+    // ---- all row loads in flight at once
+    const uint16_t *x = a.x[t] + (int64_t)b * a.sx_b[t] + (int64_t)h * a.sx_h[t] + (int64_t)row0 * a.sx_l[t] +
+                        c * SW + 8 * q;
+    const int64_t sl = a.sx_l[t];
+    uint4 xv[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        const int r = min(r0 + k * RS, n - 1);
+        xv[k] = *reinterpret_cast<const uint4 *>(x + (int64_t)r * sl);
+    }
+
+    // ---- absmax: packed 16-bit maxima of |x| (bf16 patterns with the sign
+    // cleared order like the values), reduced over the lanes sharing q
+    u16x2 m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = u16x2{0, 0};
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) absmax_item(m, xv[k]);
+#pragma unroll
+    for (int d = LPR; d < 64; d <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t o = __shfl_xor(__builtin_bit_cast(uint32_t, m[j]), d);
+            m[j] = __builtin_elementwise_max(m[j], __builtin_bit_cast(u16x2, o));
+        }
+    }
+    lds_barrier();                                 // sh_max cleared
+    if ((tid & 63) < LPR) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = __builtin_bit_cast(uint32_t, m[j]);
+            atomicMax(&sh_max[8 * q + 2 * j], w << 16);
+            atomicMax(&sh_max[8 * q + 2 * j + 1], w & 0xFFFF0000u);
+        }
+    }
+    lds_barrier();
+
+    // ---- scales of the slab's channels
+    if (tid < SW) {
+        const float mx = u2f(sh_max[tid]);
+        const float s = mx / QMAX;                 // IEEE fp32 division
+        sh_s[tid] = s;
+        sh_y[tid] = recip_for_codes(s);
+        a.scales[t][((int64_t)bh * a.G_cap + a.group_start + g) * a.D + c * SW + tid] = s;
+        if (!fast_scale_ok(s)) sh_slow = 1;
+    }
+    lds_barrier();
+
+    // ---- codes and words
+    float s8[8], y8[8];
+    {
+        const float4 *ps = reinterpret_cast<const float4 *>(sh_s + 8 * q);
+        const float4 *py = reinterpret_cast<const float4 *>(sh_y + 8 * q);
+        const float4 s0 = ps[0], s1 = ps[1], y0 = py[0], y1 = py[1];
+        s8[0] = s0.x; s8[1] = s0.y; s8[2] = s0.z; s8[3] = s0.w; s8[4] = s1.x; s8[5] = s1.y; s8[6] = s1.z; s8[7] = s1.w;
+        y8[0] = y0.x; y8[1] = y0.y; y8[2] = y0.z; y8[3] = y0.w; y8[4] = y1.x; y8[5] = y1.y; y8[6] = y1.z; y8[7] = y1.w;
+    }
+    const bool fast = __builtin_amdgcn_readfirstlane(sh_slow) == 0;
+    constexpr int CPW = 32 / BITS;
+    const int ch0 = c * SW + 8 * q;                // the lane's first channel
+    uint32_t *pk = a.packed[t] + (int64_t)bh * a.W * a.L_cap + a.tok_start + row0;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        const int r = r0 + k * RS;
+        uint32_t f[8];
+        if (fast) codes8<true>(xv[k], s8, y8, f);
+        else codes8<false>(xv[k], s8, y8, f);
+        // fields enter a word from the top (alignbit keeps the low BITS bits)
+        if constexpr (BITS == 4) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w = __builtin_amdgcn_alignbit(f[j], w, 4);
+            if (r < n) pk[(int64_t)(ch0 / CPW) * a.L_cap + r] = w;
+        } else if constexpr (BITS == 7 || BITS == 8) {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                w0 = __builtin_amdgcn_alignbit(f[j], w0, BITS);
+                w1 = __builtin_amdgcn_alignbit(f[4 + j], w1, BITS);
+            }
+            if constexpr (BITS == 7) { w0 >>= 4; w1 >>= 4; }     // 28 bits used
+            if (r < n) {
+                pk[(int64_t)(ch0 / CPW) * a.L_cap + r] = w0;
+                pk[(int64_t)(ch0 / CPW + 1) * a.L_cap + r] = w1;
+            }
+        } else {
+            // 2 bits: this lane's 8 fields are one half of a 16-channel word;
+            // the even lane of the pair (channels 16p .. 16p + 15) stores it
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w = __builtin_amdgcn_alignbit(f[j], w, 2);
+            const uint32_t half = w >> 16;
+            const uint32_t other = __shfl_xor(half, 1);
+            if ((q & 1) == 0 && r < n) pk[(int64_t)(ch0 / CPW) * a.L_cap + r] = half | (other << 16);
+        }
+    }
+}
+
+// Rows of one block that a slab work-group of nt threads holds at sw
+// channels per slab (16 row steps per thread).
+int quant_slab_max_rows(int sw, int nt) { return (nt / (sw / 8)) * 16; }
+
+template <int BITS, int SW, int NT>
+static hipError_t launch_slab_nt(const SlabArgs &a, int rpt, hipStream_t st) {
+    const int64_t grid = (a.n_units + 7) / 8 * 8;
+    if (rpt <= 4)
+        hipLaunchKernelGGL((quant_slab_kernel<BITS, SW, 4, NT>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    else if (rpt <= 8)
+        hipLaunchKernelGGL((quant_slab_kernel<BITS, SW, 8, NT>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    else if (rpt <= 16)
+        hipLaunchKernelGGL((quant_slab_kernel<BITS, SW, 16, NT>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <int BITS, int SW>
+static hipError_t launch_slab_sw(const SlabArgs &a, int rpt, int nt, hipStream_t st) {
+    if (nt == 256) return launch_slab_nt<BITS, SW, 256>(a, rpt, st);
+    if (nt == 512) return launch_slab_nt<BITS, SW, 512>(a, rpt, st);
+    if (nt == 1024) return launch_slab_nt<BITS, SW, 1024>(a, rpt, st);
+    return hipErrorInvalidValue;
+}
+
+template <int BITS>
+static hipError_t launch_slab_bits(const SlabArgs &a, int sw, int rpt, int nt, hipStream_t st) {
+    if (sw == 32) return launch_slab_sw<BITS, 32>(a, rpt, nt, st);
+    if (sw == 16) return launch_slab_sw<BITS, 16>(a, rpt, nt, st);
+    return hipErrorInvalidValue;
+}
+
+// Slab launch over the blocks [a.gb, a.gb + a.nbig) with sw channels per slab,
+// nt threads per work-group and rpt row steps per thread
+// (rows <= rpt * nt / (sw / 8)).
+hipError_t launch_quant_slab(const SlabArgs &a, int bits, int sw, int rpt, int nt, hipStream_t st) {
+    switch (bits) {
+        case 2: return launch_slab_bits<2>(a, sw, rpt, nt, st);
+        case 4: return launch_slab_bits<4>(a, sw, rpt, nt, st);
+        case 7: return launch_slab_bits<7>(a, sw, rpt, nt, st);
+        case 8: return launch_slab_bits<8>(a, sw, rpt, nt, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int BITS>
 static hipError_t launch_qp(const QuantPackArgs &a, int grid, bool split, hipStream_t st) {
     if (!split) {

@@ -4,11 +4,11 @@
 // of quantization, packing and attention runs in the gfx950 kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -18,6 +18,8 @@
 
 namespace varq {
 hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, int grid, bool split, hipStream_t st);
+hipError_t launch_quant_slab(const SlabArgs &a, int bits, int sw, int rpt, int nt, hipStream_t st);
+int quant_slab_max_rows(int sw, int nt);
 int quant_pack_resident_blocks(int bits, int lds_bytes);
 int quant_pack_max_pack();
 hipError_t launch_unpack_dequant(const UnpackArgs &a, int bits, hipStream_t st);
@@ -276,8 +278,79 @@ void qp_plan(const int32_t *off, int G, int D, QpPlan &p) {
     p.units = units;
 }
 
+// Blocks longer than a unit go to the slab kernel (no exchange, no workspace)
+// when they form a suffix [gb, G) of the call, every code word lies inside a
+// slab (bits 2, 4, 7, 8: 16, 8 or 4 codes per word) and each block's rows fit
+// a work-group's registers; the blocks before gb are whole-block units. Each
+// block takes the smallest work-group shape that holds its rows, and runs of
+// consecutive blocks of one shape are launched together.
+struct SlabRun {
+    int g0 = 0, g1 = 0, sw = 0, rpt = 0, nt = 0;
+};
+
+constexpr int kMaxSlabRuns = 16;
+
+struct SlabPlan {
+    bool use = false;
+    int gb = 0, nruns = 0;
+    SlabRun runs[kMaxSlabRuns];
+};
+
+// The work-group shape for a block of n rows: 32-channel slabs (64 B of each
+// row) where head_dim allows, else 16; 256, 512 or 1024 threads; 4, 8 or 16
+// row steps per thread. False when no shape holds n rows.
+bool slab_shape(int n, int D, SlabRun &r) {
+    static const int shapes32[][2] = {{32, 256}, {32, 512}, {16, 512}, {16, 1024}};
+    static const int shapes16[][2] = {{16, 256}, {16, 512}, {16, 1024}};
+    const bool by32 = D % 32 == 0;
+    const int ns = by32 ? 4 : 3;
+    for (int i = 0; i < ns; ++i) {
+        const int sw = by32 ? shapes32[i][0] : shapes16[i][0];
+        const int nt = by32 ? shapes32[i][1] : shapes16[i][1];
+        if (n > varq::quant_slab_max_rows(sw, nt)) continue;
+        const int rs = nt / (sw / 8);              // rows per step of a work-group
+        const int steps = (n + rs - 1) / rs;
+        r.sw = sw;
+        r.nt = nt;
+        r.rpt = steps <= 4 ? 4 : steps <= 8 ? 8 : 16;
+        return true;
+    }
+    return false;
+}
+
+SlabPlan slab_plan(const int32_t *off, int G, int D, int bits, int T) {
+    SlabPlan sp;
+    if (bits != 2 && bits != 4 && bits != 7 && bits != 8) return sp;
+    if (D % 16 != 0) return sp;
+    int gb = 0;
+    while (gb < G && off[gb + 1] - off[gb] <= T) ++gb;
+    if (gb == G) return sp;                        // no long block
+    int nruns = 0;
+    for (int g = gb; g < G; ++g) {
+        const int n = off[g + 1] - off[g];
+        if (n <= T) return sp;                     // a short block after a long one
+        SlabRun r;
+        if (!slab_shape(n, D, r)) return sp;       // too long for one work-group
+        if (nruns > 0) {
+            SlabRun &last = sp.runs[nruns - 1];
+            if (last.sw == r.sw && last.nt == r.nt && last.rpt == r.rpt) {
+                last.g1 = g + 1;
+                continue;
+            }
+        }
+        if (nruns == kMaxSlabRuns) return sp;      // too many shapes: the exchange
+        r.g0 = g;
+        r.g1 = g + 1;
+        sp.runs[nruns++] = r;
+    }
+    sp.use = true;
+    sp.gb = gb;
+    sp.nruns = nruns;
+    return sp;
+}
+
 // Workspace of a quantize+pack launch over n_tensors tensors (0 when no block
-// spans several units).
+// spans several units, or when the long blocks take the slab kernel).
 int64_t qp_plan_workspace(const QpPlan &p, int n_tensors, int B, int H, int G, int D) {
     if (p.max_nc <= 1) return 0;
     const int64_t n_units = (int64_t)n_tensors * B * H * p.units;
@@ -369,6 +442,47 @@ int qp_setup(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
 int qp_launch(varq::QuantPackArgs &a, int bits, bool split, int max_nc, void *ws, int64_t ws_bytes, void *stream) {
     const int D = a.D;
     int grid = 0;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const SlabPlan sp = split ? slab_plan(a.off, a.G, D, bits, a.chunk_rows) : SlabPlan{};
+    if (sp.use) {
+        const int nt = a.x2 ? 2 : 1;
+        if (sp.gb > 0) {
+            // the short blocks [0, gb): whole-block units, one work-group each
+            varq::QuantPackArgs pre = a;
+            pre.G = sp.gb;
+            pre.units_per_bh = a.unit_start[sp.gb];
+            pre.n_units_one = (int64_t)a.B * a.H * pre.units_per_bh;
+            pre.n_units = nt * pre.n_units_one;
+            const hipError_t e = varq::launch_quant_pack(pre, bits, (int)pre.n_units, false, st);
+            if (e != hipSuccess) return launch_status(e, "quantize_pack");
+        }
+        varq::SlabArgs sa;
+        std::memset(&sa, 0, sizeof(sa));
+        sa.x[0] = a.x; sa.sx_b[0] = a.sx_b; sa.sx_l[0] = a.sx_l; sa.sx_h[0] = a.sx_h;
+        sa.packed[0] = a.packed; sa.scales[0] = a.scales;
+        if (a.x2) {
+            sa.x[1] = a.x2; sa.sx_b[1] = a.sx2_b; sa.sx_l[1] = a.sx2_l; sa.sx_h[1] = a.sx2_h;
+            sa.packed[1] = a.packed2; sa.scales[1] = a.scales2;
+        }
+        sa.L_cap = a.L_cap; sa.tok_start = a.tok_start; sa.G_cap = a.G_cap; sa.group_start = a.group_start;
+        sa.B = a.B; sa.H = a.H; sa.D = D; sa.W = a.W;
+        for (int g = 0; g <= a.G; ++g) sa.off[g] = a.off[g];
+        // the runs of the longest blocks first
+        int order[kMaxSlabRuns];
+        for (int i = 0; i < sp.nruns; ++i) order[i] = i;
+        std::sort(order, order + sp.nruns, [&](int x, int y) {
+            const SlabRun &rx = sp.runs[x], &ry = sp.runs[y];
+            return varq::quant_slab_max_rows(rx.sw, rx.nt) * rx.rpt > varq::quant_slab_max_rows(ry.sw, ry.nt) * ry.rpt;
+        });
+        for (int i = 0; i < sp.nruns; ++i) {
+            const SlabRun &r = sp.runs[order[i]];
+            sa.gb = r.g0; sa.nbig = r.g1 - r.g0; sa.slabs = D / r.sw;
+            sa.n_units = (int64_t)nt * a.B * a.H * sa.nbig * sa.slabs;
+            const hipError_t e = varq::launch_quant_slab(sa, bits, r.sw, r.rpt, r.nt, st);
+            if (e != hipSuccess) return launch_status(e, "quantize_pack");
+        }
+        return ok();
+    }
     if (split) {
         const int64_t bhg = (int64_t)(a.x2 ? 2 : 1) * a.B * a.H * a.G;
         if (int r = check_workspace(ws, ws_bytes, qp_workspace_bytes(a.n_units, bhg, D), "quantize_pack")) return r;
@@ -446,7 +560,7 @@ int varq_quantize_pack_workspace(int B, int H, int D, int64_t L_in, const int32_
     if (int r = check_offsets(group_offsets, G_in, L_in, "quantize_pack_workspace")) return r;
     QpPlan p;
     qp_plan(group_offsets, G_in, D, p);
-    *bytes = qp_plan_workspace(p, n_tensors, B, H, G_in, D);
+    *bytes = slab_plan(group_offsets, G_in, D, bits, p.T).use ? 0 : qp_plan_workspace(p, n_tensors, B, H, G_in, D);
     return ok();
 }
 
@@ -502,7 +616,7 @@ int varq_quantize_pack_kv_noalloc(const void *k, int64_t sk_b, int64_t sk_l, int
     a.scales2 = av.scales;
     a.n_units = 2 * a.n_units_one;
     void *ws = nullptr;
-    if (split) {
+    if (split && !slab_plan(a.off, a.G, D, bits, a.chunk_rows).use) {
         const int64_t need = qp_workspace_bytes(a.n_units, (int64_t)2 * B * H * G_in, D);
         if (need > kNoallocScratchBytes)
             return fail(VARQ_EWORKSPACE,

@@ -45,6 +45,22 @@ struct QuantPackArgs {
     int32_t unit_start[VARQ_MAX_GROUPS_DEV + 1];
 };
 
+// quantize+pack of blocks longer than one work-group's unit, one work-group
+// per (tensor, batch, head, block, channel slab): the blocks [gb, G) of the
+// call (all longer than a unit), slab = SW consecutive channels. The block
+// table off[] is relative to x, as in QuantPackArgs.
+struct SlabArgs {
+    const uint16_t *x[2];       // bf16 [B, L_in, H, D] of K (and V), channel stride 1
+    int64_t sx_b[2], sx_l[2], sx_h[2];
+    uint32_t *packed[2];        // [B, H, W, L_cap]
+    float *scales[2];           // [B, H, G_cap, D]
+    int64_t L_cap, tok_start, G_cap, group_start;
+    int64_t n_units;            // n_tensors * B * H * nbig * slabs
+    int B, H, D, W;
+    int gb, nbig, slabs;        // first slab block, slab blocks, slabs per row
+    int32_t off[VARQ_MAX_GROUPS_DEV + 1];
+};
+
 struct UnpackArgs {
     const uint32_t *packed;     // [B, H, W, L_cap]
     const float *scales;        // [B, H, G_cap, D]

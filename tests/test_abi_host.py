@@ -159,27 +159,44 @@ def test_quantize_pack_workspace_query(V):
     from synth import WORKLOADS
     var = WORKLOADS["var_d30"]
     assert _qp_ws(V, var.B, var.H, var.D, list(var.offsets)) == (0, 0)      # every block fits one unit
-    # one block of 300 rows at D = 128 (128-row units): 3 chunks per (b, h)
-    r1, n1 = _qp_ws(V, 2, 3, 128, [0, 300])
+    # INT3 (10 codes per word: no whole words per channel slab), one block of
+    # 300 rows at D = 128 (128-row units): 3 chunks per (b, h) exchange maxima
+    r1, n1 = _qp_ws(V, 2, 3, 128, [0, 300], bits=3)
     assert r1 == 0 and n1 == 16 + (2 * 3 * 3 + 2 * 3 * 1) * 128 * 8
-    r2, n2 = _qp_ws(V, 2, 3, 128, [0, 300], n=2)
+    r2, n2 = _qp_ws(V, 2, 3, 128, [0, 300], bits=3, n=2)
     assert r2 == 0 and n2 == 16 + 2 * (2 * 3 * 3 + 2 * 3 * 1) * 128 * 8
     # a 4-row block packed with the 300-row block's chunks: 1 + 3 units
-    assert _qp_ws(V, 1, 1, 128, [0, 4, 304])[1] == 16 + (4 + 2) * 128 * 8
+    assert _qp_ws(V, 1, 1, 128, [0, 4, 304], bits=3)[1] == 16 + (4 + 2) * 128 * 8
     assert _qp_ws(V, 1, 1, 128, [0, 4, 304], bits=9)[0] == -2
     assert _qp_ws(V, 1, 1, 128, [0, 4, 304], n=3)[0] == -1
     assert _qp_ws(V, 1, 1, 128, [0, 4, 4])[0] == -1
+    # bits 2, 4, 7, 8 with the long blocks after the short ones: the slab
+    # kernel, no exchange (up to 8192 rows per block: 16-channel slabs, 1024
+    # threads per work-group), in at most 16 runs of one work-group shape
+    alternating = [0]
+    for i in range(17):
+        alternating.append(alternating[-1] + (300 if i % 2 else 3000))
+    for bits in (2, 4, 7, 8):
+        assert _qp_ws(V, 2, 3, 128, [0, 300], bits=bits) == (0, 0)
+        assert _qp_ws(V, 1, 1, 128, [0, 4, 304, 4400], bits=bits) == (0, 0)
+        assert _qp_ws(V, 1, 1, 128, [0, 8192], bits=bits) == (0, 0)
+        assert _qp_ws(V, 1, 1, 128, [0, 8193], bits=bits)[1] > 0            # too long for a slab
+        assert _qp_ws(V, 1, 1, 128, alternating[:17], bits=bits) == (0, 0)  # 16 runs
+        assert _qp_ws(V, 1, 1, 128, alternating, bits=bits)[1] > 0          # 17 runs
+        assert _qp_ws(V, 1, 1, 128, [0, 300, 304], bits=bits)[1] > 0        # a short block after a long one
+        assert _qp_ws(V, 1, 1, 40, [0, 1000], bits=bits)[1] > 0             # D not a multiple of 16 (408-row units)
     sf = WORKLOADS["self_forcing"]
-    r, n = _qp_ws(V, sf.B, sf.H, sf.D, [0, 1560, 3120, 4680], n=2)
+    assert _qp_ws(V, sf.B, sf.H, sf.D, [0, 1560, 3120, 4680], n=2) == (0, 0)
+    r, n = _qp_ws(V, sf.B, sf.H, sf.D, [0, 1560, 3120, 4680], bits=3, n=2)
     assert r == 0 and n == 16 + 2 * sf.B * sf.H * (3 * 13 + 3) * 128 * 8
     # the split call itself: NULL or too small a workspace is VARQ_EWORKSPACE
     kw = dict(x=0x10000, sx_b=300 * 3 * 128, sx_l=3 * 128, sx_h=128, B=2, H=3, D=128, L_in=300, off=[0, 300],
-              packed=0x20000, L_cap=304, scales=0x30000, G_cap=1)
+              packed=0x20000, L_cap=304, scales=0x30000, G_cap=1, bits=3)
     assert _qp(V, **kw) == -7 and "workspace" in V.last_error()
     assert _qp(V, ws=0x40000, ws_bytes=n1 - 8, **kw) == -7
     assert _qp(V, ws=0x40008, ws_bytes=n1, **kw) == -3           # not 16-byte aligned
     kv = dict(k=0x10000, sk_b=300 * 3 * 128, sk_l=3 * 128, sk_h=128, v=0x70000, sv_b=300 * 3 * 128,
-              sv_l=3 * 128, sv_h=128, B=2, H=3, D=128, L_in=300, off=[0, 300], L_cap=304, G_cap=1)
+              sv_l=3 * 128, sv_h=128, B=2, H=3, D=128, L_in=300, off=[0, 300], L_cap=304, G_cap=1, bits=3)
     assert _qpkv(V, ws=0x40000, ws_bytes=n1, **kv) == -7         # one tensor's worth is too small for two
     # the check accepts a NULL workspace (nothing to report)
     assert V.lib().varq_quantize_pack_check(None, None) == 0

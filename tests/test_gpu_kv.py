@@ -133,24 +133,25 @@ def test_kv_split_repeated_calls_alternating_shapes(V):
     _say("[kv split repeat]")
     g = torch.Generator(device=DEV).manual_seed(9)
     cases = []
-    for (B, L, H, D, off) in ((1, 700, 3, 128, [0, 4, 300, 700]), (2, 2000, 2, 64, [0, 900, 2000]),
-                              (1, 1560, 4, 128, [0, 1560])):
+    # INT3 takes the exchange; the INT4 case between takes the slab kernel
+    for (B, L, H, D, off, bits) in ((1, 700, 3, 128, [0, 4, 300, 700], 3), (2, 2000, 2, 64, [0, 900, 2000], 3),
+                                    (1, 1560, 4, 128, [0, 1560], 4), (1, 1560, 4, 128, [0, 1560], 3)):
         k = (torch.randn(B, L, H, D, generator=g, device=DEV) * 3).to(torch.bfloat16)
         v = torch.randn(B, L, H, D, generator=g, device=DEV).to(torch.bfloat16)
-        ref = _caches(V, B, H, D, L, len(off) - 1, 4)
-        V.quantize_pack(k, off, 4, ref[0], ref[1])
-        V.quantize_pack(v, off, 4, ref[2], ref[3])
-        cases.append((k, v, off, ref))
+        ref = _caches(V, B, H, D, L, len(off) - 1, bits)
+        V.quantize_pack(k, off, bits, ref[0], ref[1])
+        V.quantize_pack(v, off, bits, ref[2], ref[3])
+        cases.append((k, v, off, bits, ref))
     torch.cuda.synchronize()
     for rep in range(4):
-        for (k, v, off, ref) in cases:
+        for (k, v, off, bits, ref) in cases:
             B, L, H, D = k.shape
-            got = _caches(V, B, H, D, L, len(off) - 1, 4)
-            V.quantize_pack_kv(k, v, off, 4, *got)
+            got = _caches(V, B, H, D, L, len(off) - 1, bits)
+            V.quantize_pack_kv(k, v, off, bits, *got)
             V.quantize_pack_check()
             torch.cuda.synchronize()
             for a, b in zip(got, ref):
-                assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, k.shape)
+                assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, k.shape, bits)
 
 
 def test_kv_block_with_as_many_chunks_as_resident_workgroups(V):
@@ -182,3 +183,30 @@ def test_kv_block_with_as_many_chunks_as_resident_workgroups(V):
     x2 = torch.zeros(B, off2[-1], H, D, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(V.VarqError):
         V.quantize_pack_kv(x2, x2.clone(), off2, bits, *_caches(V, B, H, D, off2[-1], 2, bits))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 7, 8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_slab_blocks_at_their_limits(V, bits, D):
+    """Long blocks after short ones go to the slab kernel (one work-group per
+    block and 16- or 32-channel slab, no exchange; each block takes the
+    smallest work-group shape that holds it, runs of one shape launched
+    together): a short prefix packed into units, then blocks one row past a
+    unit, at the limits of the 256-, 512- and 1024-thread shapes and one row
+    past them, then shorter long blocks again, written at an offset of a
+    larger cache, V a strided view."""
+    _say(f"[kv slab D={D} b{bits}]")
+    T = 16384 // D
+    sizes = [3, 5, T - 1, T + 1, 1024, 1025, 2048, 2049, 4096, 4097, 8192, 1560, T + 1]
+    off = [0]
+    for n in sizes:
+        off.append(off[-1] + n)
+    assert V.quantize_pack_workspace_bytes(1, 2, D, off, bits, 2) == 0
+    g = torch.Generator().manual_seed(300 + bits + D)
+    B, L, H = 1, off[-1], 2
+    k = (torch.randn(B, L, H, D, generator=g) * 3).to(torch.bfloat16)
+    k[0, off[4]:off[5], 1, : D // 2] = 0                 # all-zero (block, channel) groups
+    big = (torch.randn(B, L, H + 1, D, generator=g) * 0.5).to(torch.bfloat16)
+    v_view = big.to(DEV)[:, :, 1:]
+    _check(V, k, v_view.cpu().contiguous(), off, bits, v_dev=v_view, tok_start=24, group_start=1,
+           extra_rows=8, extra_groups=2)

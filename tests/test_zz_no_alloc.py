@@ -1,8 +1,10 @@
 """varq_quantize_pack_kv_noalloc through the C ABI: the same words and scales,
 bit for bit, as varq_quantize_pack_kv with a workspace, on two calls in a
 row (the second smaller, reusing the fixed exchange array the first left
-behind), both with blocks longer than one work-group's rows so that the
-exchange is used; a call needing more than the fixed array is rejected."""
+behind), both at INT3 with blocks longer than one work-group's rows so that
+the exchange is used; a call needing more than the fixed array is rejected.
+A call whose long blocks take the slab kernel needs no exchange and also
+matches."""
 
 import ctypes
 import sys
@@ -49,7 +51,7 @@ def test_noalloc_equals_workspace_entry_point(V):
     g = torch.Generator(device=DEV).manual_seed(17)
     cases = [
         # (B, L, H, D, offsets, bits, tok_start, group_start, extra rows, extra groups)
-        (2, 4680, 12, 128, [0, 1560, 3120, 4680], 4, 0, 0, 0, 0),    # one next-frame block: 13 chunks per frame
+        (2, 4680, 12, 128, [0, 1560, 3120, 4680], 3, 0, 0, 0, 0),    # one next-frame block: 13 chunks per frame
         (1, 1500, 4, 64, [0, 700, 701, 1500], 3, 24, 2, 16, 1),      # smaller, at an offset of a larger cache
     ]
     for i, (B, L, H, D, off, bits, t0, g0, xr, xg) in enumerate(cases):
@@ -70,12 +72,29 @@ def test_noalloc_equals_workspace_entry_point(V):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), i
 
 
+def test_noalloc_slab_calls_match(V):
+    """INT4 next-frame block: the slab kernel, no scratch at all."""
+    g = torch.Generator(device=DEV).manual_seed(23)
+    B, L, H, D, off, bits = 2, 4680, 4, 128, [0, 1560, 3120, 4680], 4
+    k = (torch.randn(B, L, H, D, generator=g, device=DEV) * 3).to(torch.bfloat16)
+    v = torch.randn(B, L, H, D, generator=g, device=DEV).to(torch.bfloat16)
+    assert V.quantize_pack_workspace_bytes(B, H, D, off, bits, 2) == 0
+    ref = _caches(V, B, H, D, L, 3, bits)
+    V.quantize_pack_kv(k, v, off, bits, *ref)
+    got = _caches(V, B, H, D, L, 3, bits)
+    assert _noalloc(V, k, v, off, bits, got) == 0, V.last_error()
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_noalloc_rejects_calls_beyond_the_fixed_array(V):
-    """Infinity-8B-like K+V over all 13 scales needs ~45 MB of exchange state:
-    rejected with VARQ_EWORKSPACE before anything is launched (outputs untouched)."""
+    """Infinity-8B-like K+V over all 13 scales at INT3 needs ~45 MB of exchange
+    state: rejected with VARQ_EWORKSPACE before anything is launched (outputs
+    untouched)."""
     from synth import WORKLOADS
     wl = WORKLOADS["infinity_8b"]
-    B, H, D, bits = wl.B, wl.H, wl.D, 4
+    B, H, D, bits = wl.B, wl.H, wl.D, 3
     off = list(wl.offsets)
     assert V.quantize_pack_workspace_bytes(B, H, D, off, bits, 2) > 16 << 20
     k = torch.zeros(B, wl.L, H, D, dtype=torch.bfloat16, device=DEV)
