@@ -508,23 +508,12 @@ def main():
             print(f"bench.py: quantize+pack exchange check failed {when}: {e}", file=sys.stderr)
             sys.exit(3)
 
-    for _ in range(args.warmup):            # also allocates the calls' workspaces
-        step()
-    torch.cuda.synchronize()
-    # timed region: K steps, wall clock between two synchronizations, no events
-    # inside (each timing event leaves the GPU idle for a few microseconds)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = dt * 1e3 / args.steps
-    exchange_check("after the timed steps")
-
-    # kernel times: the same K steps again with only one kernel's launches,
-    # back to back on the launch stream, between two events (the attention
+    # per-kernel times: the K steps rerun with only one kernel's launches,
+    # back to back on the launch stream between two events (the attention
     # calls read the cache the step wrote; re-quantizing a block rewrites the
-    # same words)
+    # same words), once just before and once just after the timed steps: the
+    # clock drifts with the board's power and temperature, and the mean of
+    # the two passes brackets the timed region
     def kind_ms(kind):
         if not any((st[0] == "qp") == (kind == "qp") for st in launches):
             return 0.0
@@ -537,8 +526,23 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    qp_step_ms = kind_ms("qp")
-    at_step_ms = kind_ms("attn")
+    for _ in range(args.warmup):            # also allocates the calls' workspaces
+        step()
+    torch.cuda.synchronize()
+    pre = (kind_ms("qp"), kind_ms("attn"))  # the cache stays as the steps leave it
+    # timed region: K steps, wall clock between two synchronizations, no events
+    # inside (each timing event leaves the GPU idle for a few microseconds)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+    exchange_check("after the timed steps")
+
+    post = (kind_ms("qp"), kind_ms("attn"))
+    qp_step_ms = 0.5 * (pre[0] + post[0])
+    at_step_ms = 0.5 * (pre[1] + post[1])
     exchange_check("after the per-kernel passes")
     n_qp_per_step = max(1, len(qp_b))
     n_at_per_step = max(1, len(at_b))
@@ -553,12 +557,15 @@ def main():
 
     kernels = {
         "timing": "per kernel: the K steps rerun with only that kernel's launches, back to back, between two "
-                  "HIP events; avg_ms = that time / launches; step_ms = that time per step",
+                  "HIP events, once just before and once just after the timed steps; step_ms = the mean of the "
+                  "two per step (step_ms_before/after: each pass), avg_ms = step_ms / launches",
         "quant_pack": {"avg_ms": round(qp_avg_ms, 5), "step_ms": round(qp_step_ms, 5),
+                       "step_ms_before": round(pre[0], 5), "step_ms_after": round(post[0], 5),
                        "launches_per_step": len(qp_b),
                        "alg_bytes_per_launch": int(qp_bytes_per_launch), "GB/s": round(qp_gbs, 1),
                        "hbm_frac": round(qp_gbs / HBM_PEAK_GBS, 4)},
         "packed_attention": {"avg_ms": round(at_avg_ms, 5), "step_ms": round(at_step_ms, 5),
+                             "step_ms_before": round(pre[1], 5), "step_ms_after": round(post[1], 5),
                              "launches_per_step": len(at_b),
                              "alg_bytes_per_launch": int(at_bytes_per_launch),
                              "alg_flops_per_launch": at_flops_per_launch,

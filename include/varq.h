@@ -109,11 +109,13 @@ int varq_cache_bytes(int B, int H, int head_dim, int64_t L_cap, int64_t G_cap, i
  * block of more 16384-element chunks than resident work-groups, or a token
  * stride or cache length beyond 32-bit byte offsets), VARQ_ELAUNCH.
  * Long blocks: a block longer than one work-group's 16384 elements (16384 / D
- * token rows) is handled whole by one work-group per 16- or 32-channel slab
- * when the long blocks follow all the short ones, bits is 2, 4, 7 or 8, D is
- * a multiple of 16, no block exceeds 8192 rows and the long blocks form at
- * most 16 runs of consecutive blocks that take one work-group shape (each
- * block takes the smallest that holds it); such calls need no workspace. Otherwise its chunks exchange per-channel
+ * token rows) is handled whole by one work-group per channel slab when the
+ * long blocks follow all the short ones and form at most 16 runs of
+ * consecutive blocks that take one work-group shape (each block takes the
+ * smallest that holds it), and either bits is 2, 4, 7 or 8, D a multiple of
+ * 16 and no block over 8192 rows (16- or 32-channel slabs), or bits is 3, 5
+ * or 6 and no block over 1612, 2688, 1612 rows (40-, 24-, 40-channel slabs,
+ * any D); such calls need no workspace. Otherwise its chunks exchange per-channel
  * maxima through the caller's workspace (varq_quantize_pack_workspace gives
  * the size: 16 bytes of launch state plus 8 bytes per (chunk, channel) and per
  * (block, channel); it is 0 when no exchange is needed, and workspace may then

@@ -45,6 +45,7 @@
 // those work-groups end round k, publish their chunks of A, r's gather ends
 // and A's chunks in round k end too. So every work-group ends round k. Spins
 // are nevertheless bounded and report a timeout through a status word.
+#include <algorithm>
 #include <mutex>
 
 #include "varq_device.h"
@@ -846,6 +847,146 @@ __global__ __launch_bounds__(NT) void quant_slab_kernel(const SlabArgs a) {
     }
 }
 
+// Slab width at 3, 5 and 6 bits: the least multiple of 8 channels (one lane's
+// 16-byte load) that is also a multiple of the codes per word (10, 6, 5), so
+// every slab starts on a word boundary; the last slab of a row takes the
+// remaining D mod width channels (a multiple of 8, whole words up to the row's
+// last, partial word).
+constexpr int staged_slab_width(int bits) { return bits == 5 ? 24 : 40; }
+
+// quantize+pack of whole long blocks at 3, 5 or 6 bits, one work-group per
+// (tensor, batch, head, block, slab), with no exchange: words straddle the
+// lanes' 8-channel loads, so the codes go through LDS as bytes ([row][slab]
+// in dynamic LDS, rows * width bytes) and words are assembled from there.
+template <int BITS, int RPT, int NT>
+__global__ __launch_bounds__(NT) void quant_slab_staged_kernel(const SlabArgs a) {
+    static_assert(BITS == 3 || BITS == 5 || BITS == 6, "codes straddle the lanes' channel octets");
+    constexpr int CPW = 32 / BITS;
+    constexpr int SW = staged_slab_width(BITS);
+    constexpr int WSMAX = (SW + CPW - 1) / CPW;
+    constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
+    extern __shared__ __attribute__((aligned(16))) uint8_t sh_codes[];
+    __shared__ uint32_t sh_max[SW];
+    __shared__ __attribute__((aligned(16))) float sh_s[SW];
+    __shared__ __attribute__((aligned(16))) float sh_y[SW];
+    __shared__ uint32_t sh_slow;
+
+    const int64_t lid = xcd_logical_id(blockIdx.x, a.n_units);
+    if (lid < 0) return;
+    const int c = (int)(lid % a.slabs);
+    int64_t v = lid / a.slabs;
+    const int jr = (int)(v % a.nbig);
+    v /= a.nbig;
+    const int bh = (int)(v % ((int64_t)a.B * a.H));
+    const int t = (int)(v / ((int64_t)a.B * a.H));
+    const int g = a.gb + (a.nbig - 1 - jr);
+    const int row0 = a.off[g], n = a.off[g + 1] - row0;
+    const int b = bh / a.H, h = bh % a.H;
+
+    const int ch0 = c * SW;
+    const int width = min(SW, a.D - ch0);          // a multiple of 8
+    const int lpr = width >> 3;                    // lanes per row
+    const int rs = NT / lpr;                       // rows per step
+    const int steps = (n + rs - 1) / rs;           // <= RPT (checked on the host)
+    const int tid = threadIdx.x;
+    const int q = tid % lpr, r0 = tid / lpr;
+    const bool active = r0 < rs;
+    if (tid < SW) sh_max[tid] = 0;
+    if (tid == 0) sh_slow = 0;
+
+    // ---- all row loads in flight at once (rows past n re-read row n - 1)
+    const uint16_t *x = a.x[t] + (int64_t)b * a.sx_b[t] + (int64_t)h * a.sx_h[t] + (int64_t)row0 * a.sx_l[t] +
+                        ch0 + 8 * q;
+    const int64_t sl = a.sx_l[t];
+    uint4 xv[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        xv[k] = make_uint4(0, 0, 0, 0);
+        if (active && k < steps) {
+            const int r = min(r0 + k * rs, n - 1);
+            xv[k] = *reinterpret_cast<const uint4 *>(x + (int64_t)r * sl);
+        }
+    }
+
+    // ---- absmax per channel: the lane's rows, then LDS max-atomics
+    u16x2 m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = u16x2{0, 0};
+#pragma unroll
+    for (int k = 0; k < RPT; ++k)
+        if (k < steps) absmax_item(m, xv[k]);      // zero for inactive lanes
+    lds_barrier();                                 // sh_max cleared
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = __builtin_bit_cast(uint32_t, m[j]);
+            atomicMax(&sh_max[8 * q + 2 * j], w << 16);
+            atomicMax(&sh_max[8 * q + 2 * j + 1], w & 0xFFFF0000u);
+        }
+    }
+    lds_barrier();
+
+    // ---- scales of the slab's channels
+    if (tid < width) {
+        const float mx = u2f(sh_max[tid]);
+        const float sc = mx / QMAX;                // IEEE fp32 division
+        sh_s[tid] = sc;
+        sh_y[tid] = recip_for_codes(sc);
+        a.scales[t][((int64_t)bh * a.G_cap + a.group_start + g) * a.D + ch0 + tid] = sc;
+        if (!fast_scale_ok(sc)) sh_slow = 1;
+    }
+    lds_barrier();
+
+    // ---- codes as bytes into LDS, row r of the slab at r * SW
+    if (active) {
+        float s8[8], y8[8];
+        const float4 *ps = reinterpret_cast<const float4 *>(sh_s + 8 * q);
+        const float4 *py = reinterpret_cast<const float4 *>(sh_y + 8 * q);
+        const float4 s0 = ps[0], s1 = ps[1], y0 = py[0], y1 = py[1];
+        s8[0] = s0.x; s8[1] = s0.y; s8[2] = s0.z; s8[3] = s0.w; s8[4] = s1.x; s8[5] = s1.y; s8[6] = s1.z; s8[7] = s1.w;
+        y8[0] = y0.x; y8[1] = y0.y; y8[2] = y0.z; y8[3] = y0.w; y8[4] = y1.x; y8[5] = y1.y; y8[6] = y1.z; y8[7] = y1.w;
+        const bool fast = __builtin_amdgcn_readfirstlane(sh_slow) == 0;
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            const int r = r0 + k * rs;
+            if (k < steps && r < n) {
+                uint32_t f[8];
+                if (fast) codes8<true>(xv[k], s8, y8, f);
+                else codes8<false>(xv[k], s8, y8, f);
+                const uint32_t lo = (f[0] & 0xFFu) | ((f[1] & 0xFFu) << 8) | ((f[2] & 0xFFu) << 16) | (f[3] << 24);
+                const uint32_t hi = (f[4] & 0xFFu) | ((f[5] & 0xFFu) << 8) | ((f[6] & 0xFFu) << 16) | (f[7] << 24);
+                *reinterpret_cast<uint2 *>(sh_codes + r * SW + 8 * q) = make_uint2(lo, hi);
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- words: word wi of the slab holds its codes wi*CPW .. (from the low
+    // bits up); consecutive threads take consecutive rows of one word plane
+    const int ws = (width + CPW - 1) / CPW;
+    uint32_t *pk = a.packed[t] + ((int64_t)bh * a.W + ch0 / CPW) * a.L_cap + a.tok_start + row0;
+#pragma unroll
+    for (int wi = 0; wi < WSMAX; ++wi) {
+        if (wi >= ws) break;
+        const int start = wi * CPW;                // first code byte of the word in the row
+        const int nc = min(CPW, width - start);
+        const int base8 = start & ~7, off = start & 7;
+        for (int r = tid; r < n; r += NT) {
+            const uint8_t *row = sh_codes + r * SW + base8;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(row);
+            const uint2 hi = (off + CPW > 8) ? *reinterpret_cast<const uint2 *>(row + 8) : make_uint2(0, 0);
+            const uint32_t d[4] = {lo.x, lo.y, hi.x, hi.y};
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) {
+                const int byte = off + j;
+                if (j < nc) w |= __builtin_amdgcn_ubfe(d[byte >> 2], 8 * (byte & 3), BITS) << (BITS * j);
+            }
+            pk[(int64_t)wi * a.L_cap + r] = w;
+        }
+    }
+}
+
 // Rows of one block that a slab work-group of nt threads holds at sw
 // channels per slab (16 row steps per thread).
 int quant_slab_max_rows(int sw, int nt) { return (nt / (sw / 8)) * 16; }
@@ -877,6 +1018,51 @@ static hipError_t launch_slab_bits(const SlabArgs &a, int sw, int rpt, int nt, h
     if (sw == 32) return launch_slab_sw<BITS, 32>(a, rpt, nt, st);
     if (sw == 16) return launch_slab_sw<BITS, 16>(a, rpt, nt, st);
     return hipErrorInvalidValue;
+}
+
+// Rows of one block that a staged slab work-group of nt threads holds at 3,
+// 5 or 6 bits (16 row steps per thread of the full slab width, and the codes
+// of every row in 63 KB of dynamic LDS, within the 64 KB a launch gets
+// without an attribute).
+int quant_slab_staged_max_rows(int bits, int nt) {
+    const int sw = staged_slab_width(bits);
+    return std::min((nt / (sw / 8)) * 16, 64512 / sw);
+}
+
+int quant_slab_staged_width(int bits) { return staged_slab_width(bits); }
+
+template <int BITS, int NT>
+static hipError_t launch_staged_nt(const SlabArgs &a, int rpt, int max_rows, hipStream_t st) {
+    const int64_t grid = (a.n_units + 7) / 8 * 8;
+    const size_t lds = (size_t)max_rows * staged_slab_width(BITS);
+    if (rpt <= 4)
+        hipLaunchKernelGGL((quant_slab_staged_kernel<BITS, 4, NT>), dim3((unsigned)grid), dim3(NT), lds, st, a);
+    else if (rpt <= 8)
+        hipLaunchKernelGGL((quant_slab_staged_kernel<BITS, 8, NT>), dim3((unsigned)grid), dim3(NT), lds, st, a);
+    else if (rpt <= 16)
+        hipLaunchKernelGGL((quant_slab_staged_kernel<BITS, 16, NT>), dim3((unsigned)grid), dim3(NT), lds, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t launch_staged_bits(const SlabArgs &a, int rpt, int nt, int max_rows, hipStream_t st) {
+    if (nt == 256) return launch_staged_nt<BITS, 256>(a, rpt, max_rows, st);
+    if (nt == 512) return launch_staged_nt<BITS, 512>(a, rpt, max_rows, st);
+    if (nt == 1024) return launch_staged_nt<BITS, 1024>(a, rpt, max_rows, st);
+    return hipErrorInvalidValue;
+}
+
+// Staged slab launch (3, 5 or 6 bits) over the blocks [a.gb, a.gb + a.nbig),
+// the longest of max_rows rows.
+hipError_t launch_quant_slab_staged(const SlabArgs &a, int bits, int rpt, int nt, int max_rows, hipStream_t st) {
+    switch (bits) {
+        case 3: return launch_staged_bits<3>(a, rpt, nt, max_rows, st);
+        case 5: return launch_staged_bits<5>(a, rpt, nt, max_rows, st);
+        case 6: return launch_staged_bits<6>(a, rpt, nt, max_rows, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // Slab launch over the blocks [a.gb, a.gb + a.nbig) with sw channels per slab,

@@ -20,6 +20,9 @@ namespace varq {
 hipError_t launch_quant_pack(const QuantPackArgs &a, int bits, int grid, bool split, hipStream_t st);
 hipError_t launch_quant_slab(const SlabArgs &a, int bits, int sw, int rpt, int nt, hipStream_t st);
 int quant_slab_max_rows(int sw, int nt);
+hipError_t launch_quant_slab_staged(const SlabArgs &a, int bits, int rpt, int nt, int max_rows, hipStream_t st);
+int quant_slab_staged_max_rows(int bits, int nt);
+int quant_slab_staged_width(int bits);
 int quant_pack_resident_blocks(int bits, int lds_bytes);
 int quant_pack_max_pack();
 hipError_t launch_unpack_dequant(const UnpackArgs &a, int bits, hipStream_t st);
@@ -279,22 +282,32 @@ void qp_plan(const int32_t *off, int G, int D, QpPlan &p) {
 }
 
 // Blocks longer than a unit go to the slab kernel (no exchange, no workspace)
-// when they form a suffix [gb, G) of the call, every code word lies inside a
-// slab (bits 2, 4, 7, 8: 16, 8 or 4 codes per word) and each block's rows fit
-// a work-group's registers; the blocks before gb are whole-block units. Each
-// block takes the smallest work-group shape that holds its rows, and runs of
-// consecutive blocks of one shape are launched together.
+// when they form a suffix [gb, G) of the call and each block's rows fit one
+// work-group: at bits 2, 4, 7 and 8 (16, 8 or 4 codes per word, head_dim a
+// multiple of 16) every word lies inside a 16- or 32-channel slab and is
+// assembled in registers; at 3, 5 and 6 bits the slab is 40, 24 or 40
+// channels (word boundaries that are also 8-channel boundaries) and the codes
+// go through LDS. The blocks before gb are whole-block units. Each block takes
+// the smallest work-group shape that holds its rows, and runs of consecutive
+// blocks of one shape are launched together.
 struct SlabRun {
     int g0 = 0, g1 = 0, sw = 0, rpt = 0, nt = 0;
+    int max_rows = 0;       // the run's longest block
 };
 
 constexpr int kMaxSlabRuns = 16;
 
 struct SlabPlan {
     bool use = false;
+    bool staged = false;    // 3, 5, 6 bits
     int gb = 0, nruns = 0;
     SlabRun runs[kMaxSlabRuns];
 };
+
+bool staged_bits(int bits) { return bits == 3 || bits == 5 || bits == 6; }
+
+// Rows a work-group of a run's shape holds.
+int slab_capacity(const SlabRun &r) { return r.nt / (r.sw / 8) * r.rpt; }
 
 // The work-group shape for a block of n rows: 32-channel slabs (64 B of each
 // row) where head_dim allows, else 16; 256, 512 or 1024 threads; 4, 8 or 16
@@ -318,10 +331,27 @@ bool slab_shape(int n, int D, SlabRun &r) {
     return false;
 }
 
+// The same at 3, 5 and 6 bits (fixed slab width; rows also bounded by the
+// 64 KB of LDS that hold their codes).
+bool staged_shape(int n, int bits, SlabRun &r) {
+    const int sw = varq::quant_slab_staged_width(bits);
+    for (int nt : {256, 512, 1024}) {
+        if (n > varq::quant_slab_staged_max_rows(bits, nt)) continue;
+        const int rs = nt / (sw / 8);
+        const int steps = (n + rs - 1) / rs;
+        r.sw = sw;
+        r.nt = nt;
+        r.rpt = steps <= 4 ? 4 : steps <= 8 ? 8 : 16;
+        return true;
+    }
+    return false;
+}
+
 SlabPlan slab_plan(const int32_t *off, int G, int D, int bits, int T) {
     SlabPlan sp;
-    if (bits != 2 && bits != 4 && bits != 7 && bits != 8) return sp;
-    if (D % 16 != 0) return sp;
+    sp.staged = staged_bits(bits);
+    if (!sp.staged && (bits != 2 && bits != 4 && bits != 7 && bits != 8)) return sp;
+    if (!sp.staged && D % 16 != 0) return sp;
     int gb = 0;
     while (gb < G && off[gb + 1] - off[gb] <= T) ++gb;
     if (gb == G) return sp;                        // no long block
@@ -330,17 +360,19 @@ SlabPlan slab_plan(const int32_t *off, int G, int D, int bits, int T) {
         const int n = off[g + 1] - off[g];
         if (n <= T) return sp;                     // a short block after a long one
         SlabRun r;
-        if (!slab_shape(n, D, r)) return sp;       // too long for one work-group
+        if (!(sp.staged ? staged_shape(n, bits, r) : slab_shape(n, D, r))) return sp;   // too long
         if (nruns > 0) {
             SlabRun &last = sp.runs[nruns - 1];
             if (last.sw == r.sw && last.nt == r.nt && last.rpt == r.rpt) {
                 last.g1 = g + 1;
+                last.max_rows = std::max(last.max_rows, n);
                 continue;
             }
         }
         if (nruns == kMaxSlabRuns) return sp;      // too many shapes: the exchange
         r.g0 = g;
         r.g1 = g + 1;
+        r.max_rows = n;
         sp.runs[nruns++] = r;
     }
     sp.use = true;
@@ -471,14 +503,14 @@ int qp_launch(varq::QuantPackArgs &a, int bits, bool split, int max_nc, void *ws
         int order[kMaxSlabRuns];
         for (int i = 0; i < sp.nruns; ++i) order[i] = i;
         std::sort(order, order + sp.nruns, [&](int x, int y) {
-            const SlabRun &rx = sp.runs[x], &ry = sp.runs[y];
-            return varq::quant_slab_max_rows(rx.sw, rx.nt) * rx.rpt > varq::quant_slab_max_rows(ry.sw, ry.nt) * ry.rpt;
+            return slab_capacity(sp.runs[x]) > slab_capacity(sp.runs[y]);
         });
         for (int i = 0; i < sp.nruns; ++i) {
             const SlabRun &r = sp.runs[order[i]];
-            sa.gb = r.g0; sa.nbig = r.g1 - r.g0; sa.slabs = D / r.sw;
+            sa.gb = r.g0; sa.nbig = r.g1 - r.g0; sa.slabs = (D + r.sw - 1) / r.sw;
             sa.n_units = (int64_t)nt * a.B * a.H * sa.nbig * sa.slabs;
-            const hipError_t e = varq::launch_quant_slab(sa, bits, r.sw, r.rpt, r.nt, st);
+            const hipError_t e = sp.staged ? varq::launch_quant_slab_staged(sa, bits, r.rpt, r.nt, r.max_rows, st)
+                                           : varq::launch_quant_slab(sa, bits, r.sw, r.rpt, r.nt, st);
             if (e != hipSuccess) return launch_status(e, "quantize_pack");
         }
         return ok();

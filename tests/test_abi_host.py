@@ -159,14 +159,15 @@ def test_quantize_pack_workspace_query(V):
     from synth import WORKLOADS
     var = WORKLOADS["var_d30"]
     assert _qp_ws(V, var.B, var.H, var.D, list(var.offsets)) == (0, 0)      # every block fits one unit
-    # INT3 (10 codes per word: no whole words per channel slab), one block of
-    # 300 rows at D = 128 (128-row units): 3 chunks per (b, h) exchange maxima
-    r1, n1 = _qp_ws(V, 2, 3, 128, [0, 300], bits=3)
-    assert r1 == 0 and n1 == 16 + (2 * 3 * 3 + 2 * 3 * 1) * 128 * 8
-    r2, n2 = _qp_ws(V, 2, 3, 128, [0, 300], bits=3, n=2)
-    assert r2 == 0 and n2 == 16 + 2 * (2 * 3 * 3 + 2 * 3 * 1) * 128 * 8
-    # a 4-row block packed with the 300-row block's chunks: 1 + 3 units
-    assert _qp_ws(V, 1, 1, 128, [0, 4, 304], bits=3)[1] == 16 + (4 + 2) * 128 * 8
+    # INT3 with a block longer than the staged slab kernel holds (1612 rows at
+    # 40-channel slabs): 1700 rows at D = 128 (128-row units) are 14 chunks
+    # per (b, h) that exchange maxima
+    r1, n1 = _qp_ws(V, 2, 3, 128, [0, 1700], bits=3)
+    assert r1 == 0 and n1 == 16 + (2 * 3 * 14 + 2 * 3 * 1) * 128 * 8
+    r2, n2 = _qp_ws(V, 2, 3, 128, [0, 1700], bits=3, n=2)
+    assert r2 == 0 and n2 == 16 + 2 * (2 * 3 * 14 + 2 * 3 * 1) * 128 * 8
+    # a 4-row block before it takes a unit of its own: 1 + 14 units, 2 blocks
+    assert _qp_ws(V, 1, 1, 128, [0, 4, 1704], bits=3)[1] == 16 + (15 + 2) * 128 * 8
     assert _qp_ws(V, 1, 1, 128, [0, 4, 304], bits=9)[0] == -2
     assert _qp_ws(V, 1, 1, 128, [0, 4, 304], n=3)[0] == -1
     assert _qp_ws(V, 1, 1, 128, [0, 4, 4])[0] == -1
@@ -185,18 +186,27 @@ def test_quantize_pack_workspace_query(V):
         assert _qp_ws(V, 1, 1, 128, alternating, bits=bits)[1] > 0          # 17 runs
         assert _qp_ws(V, 1, 1, 128, [0, 300, 304], bits=bits)[1] > 0        # a short block after a long one
         assert _qp_ws(V, 1, 1, 40, [0, 1000], bits=bits)[1] > 0             # D not a multiple of 16 (408-row units)
+    # bits 3, 5, 6: the staged slab kernel (40-, 24-, 40-channel slabs, codes
+    # through LDS) up to 1612, 2688, 1612 rows per block, any head_dim
+    for bits, limit in ((3, 1612), (5, 2688), (6, 1612)):
+        assert _qp_ws(V, 2, 3, 128, [0, 300], bits=bits) == (0, 0)
+        assert _qp_ws(V, 1, 1, 128, [0, 4, 304, 4 + 300 + limit], bits=bits) == (0, 0)
+        assert _qp_ws(V, 1, 1, 128, [0, limit + 1], bits=bits)[1] > 0      # too long for a slab
+        assert _qp_ws(V, 1, 1, 128, [0, 300, 304], bits=bits)[1] > 0        # a short block after a long one
+        assert _qp_ws(V, 1, 1, 40, [0, 1000], bits=bits) == (0, 0)          # one partial-width slab
     sf = WORKLOADS["self_forcing"]
     assert _qp_ws(V, sf.B, sf.H, sf.D, [0, 1560, 3120, 4680], n=2) == (0, 0)
-    r, n = _qp_ws(V, sf.B, sf.H, sf.D, [0, 1560, 3120, 4680], bits=3, n=2)
-    assert r == 0 and n == 16 + 2 * sf.B * sf.H * (3 * 13 + 3) * 128 * 8
+    assert _qp_ws(V, sf.B, sf.H, sf.D, [0, 1560, 3120, 4680], bits=3, n=2) == (0, 0)
+    r, n = _qp_ws(V, sf.B, sf.H, sf.D, [0, 1560, 3120, 4680, 4684], bits=3, n=2)   # a short block last
+    assert r == 0 and n > 0
     # the split call itself: NULL or too small a workspace is VARQ_EWORKSPACE
-    kw = dict(x=0x10000, sx_b=300 * 3 * 128, sx_l=3 * 128, sx_h=128, B=2, H=3, D=128, L_in=300, off=[0, 300],
-              packed=0x20000, L_cap=304, scales=0x30000, G_cap=1, bits=3)
+    kw = dict(x=0x10000, sx_b=1700 * 3 * 128, sx_l=3 * 128, sx_h=128, B=2, H=3, D=128, L_in=1700, off=[0, 1700],
+              packed=0x20000, L_cap=1704, scales=0x30000, G_cap=1, bits=3)
     assert _qp(V, **kw) == -7 and "workspace" in V.last_error()
     assert _qp(V, ws=0x40000, ws_bytes=n1 - 8, **kw) == -7
     assert _qp(V, ws=0x40008, ws_bytes=n1, **kw) == -3           # not 16-byte aligned
-    kv = dict(k=0x10000, sk_b=300 * 3 * 128, sk_l=3 * 128, sk_h=128, v=0x70000, sv_b=300 * 3 * 128,
-              sv_l=3 * 128, sv_h=128, B=2, H=3, D=128, L_in=300, off=[0, 300], L_cap=304, G_cap=1, bits=3)
+    kv = dict(k=0x10000, sk_b=1700 * 3 * 128, sk_l=3 * 128, sk_h=128, v=0x70000, sv_b=1700 * 3 * 128,
+              sv_l=3 * 128, sv_h=128, B=2, H=3, D=128, L_in=1700, off=[0, 1700], L_cap=1704, G_cap=1, bits=3)
     assert _qpkv(V, ws=0x40000, ws_bytes=n1, **kv) == -7         # one tensor's worth is too small for two
     # the check accepts a NULL workspace (nothing to report)
     assert V.lib().varq_quantize_pack_check(None, None) == 0

@@ -84,16 +84,20 @@ def test_kv_placement_and_strides(V):
 
 
 def test_kv_split_blocks(V):
-    """Blocks longer than one work-group's rows (head_dim 128: 128 rows) take the
-    cooperative kernel, once per tensor."""
+    """Blocks longer than one work-group's rows (head_dim 128: 128 rows) that
+    cannot take a slab kernel (a short block after a long one) take the
+    cooperative kernel with its exchange, once per tensor."""
     _say("[kv split]")
     g = torch.Generator().manual_seed(6)
     B, L, H, D = 1, 700, 3, 128
     k = (torch.randn(B, L, H, D, generator=g) * 2).to(torch.bfloat16)
     v = torch.randn(B, L, H, D, generator=g).to(torch.bfloat16)
-    _check(V, k, v, [0, 4, 300, 700], 4)
+    off = [0, 300, 304, 700]
+    for bits in (4, 3):
+        assert V.quantize_pack_workspace_bytes(B, H, D, off, bits, 2) > 0
+    _check(V, k, v, off, 4)
     # the same blocks appended at an offset of a larger cache
-    _check(V, k, v, [0, 4, 300, 700], 3, tok_start=40, group_start=2, extra_rows=24, extra_groups=1)
+    _check(V, k, v, off, 3, tok_start=40, group_start=2, extra_rows=24, extra_groups=1)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -133,9 +137,11 @@ def test_kv_split_repeated_calls_alternating_shapes(V):
     _say("[kv split repeat]")
     g = torch.Generator(device=DEV).manual_seed(9)
     cases = []
-    # INT3 takes the exchange; the INT4 case between takes the slab kernel
-    for (B, L, H, D, off, bits) in ((1, 700, 3, 128, [0, 4, 300, 700], 3), (2, 2000, 2, 64, [0, 900, 2000], 3),
-                                    (1, 1560, 4, 128, [0, 1560], 4), (1, 1560, 4, 128, [0, 1560], 3)):
+    # INT3 blocks over 1612 rows take the exchange; the INT4 case between
+    # takes the slab kernel
+    for (B, L, H, D, off, bits) in ((1, 2000, 3, 128, [0, 4, 300, 2000], 3), (2, 2000, 2, 64, [0, 1800, 2000], 3),
+                                    (1, 1560, 4, 128, [0, 1560], 4), (1, 1700, 4, 128, [0, 1700], 3)):
+        assert (V.quantize_pack_workspace_bytes(B, H, D, off, bits, 2) > 0) == (bits == 3)
         k = (torch.randn(B, L, H, D, generator=g, device=DEV) * 3).to(torch.bfloat16)
         v = torch.randn(B, L, H, D, generator=g, device=DEV).to(torch.bfloat16)
         ref = _caches(V, B, H, D, L, len(off) - 1, bits)
@@ -203,6 +209,35 @@ def test_kv_slab_blocks_at_their_limits(V, bits, D):
         off.append(off[-1] + n)
     assert V.quantize_pack_workspace_bytes(1, 2, D, off, bits, 2) == 0
     g = torch.Generator().manual_seed(300 + bits + D)
+    B, L, H = 1, off[-1], 2
+    k = (torch.randn(B, L, H, D, generator=g) * 3).to(torch.bfloat16)
+    k[0, off[4]:off[5], 1, : D // 2] = 0                 # all-zero (block, channel) groups
+    big = (torch.randn(B, L, H + 1, D, generator=g) * 0.5).to(torch.bfloat16)
+    v_view = big.to(DEV)[:, :, 1:]
+    _check(V, k, v_view.cpu().contiguous(), off, bits, v_dev=v_view, tok_start=24, group_start=1,
+           extra_rows=8, extra_groups=2)
+
+
+@pytest.mark.parametrize("bits", [3, 5, 6])
+@pytest.mark.parametrize("D", [40, 64, 128])
+def test_kv_staged_slab_blocks_at_their_limits(V, bits, D):
+    """At 3, 5 and 6 bits long blocks after short ones go to the staged slab
+    kernel (40-, 24-, 40-channel slabs whose words are assembled from code
+    bytes in LDS; the last slab of a row takes the remaining channels): a short
+    prefix, blocks one row past a unit, at the 256-thread shape's limit and one
+    past it, at the largest block it takes, a frame, written at an offset of a
+    larger cache, V a strided view."""
+    _say(f"[kv staged slab D={D} b{bits}]")
+    T = 16384 // D
+    sw = 24 if bits == 5 else 40
+    r256 = (256 // (sw // 8)) * 16
+    limit = min((512 // (sw // 8)) * 16, 64512 // sw)
+    sizes = [3, 5, T - 1, T + 1, r256, r256 + 1, limit, 1560, T + 1]
+    off = [0]
+    for n in sizes:
+        off.append(off[-1] + n)
+    assert V.quantize_pack_workspace_bytes(1, 2, D, off, bits, 2) == 0
+    g = torch.Generator().manual_seed(400 + bits + D)
     B, L, H = 1, off[-1], 2
     k = (torch.randn(B, L, H, D, generator=g) * 3).to(torch.bfloat16)
     k[0, off[4]:off[5], 1, : D // 2] = 0                 # all-zero (block, channel) groups

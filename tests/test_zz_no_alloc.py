@@ -1,8 +1,9 @@
 """varq_quantize_pack_kv_noalloc through the C ABI: the same words and scales,
 bit for bit, as varq_quantize_pack_kv with a workspace, on two calls in a
 row (the second smaller, reusing the fixed exchange array the first left
-behind), both at INT3 with blocks longer than one work-group's rows so that
-the exchange is used; a call needing more than the fixed array is rejected.
+behind), both at INT3 with blocks that no slab kernel takes (over 1612 rows,
+or a short block after a long one) so that the exchange is used; a call
+needing more than the fixed array is rejected.
 A call whose long blocks take the slab kernel needs no exchange and also
 matches."""
 
@@ -51,7 +52,7 @@ def test_noalloc_equals_workspace_entry_point(V):
     g = torch.Generator(device=DEV).manual_seed(17)
     cases = [
         # (B, L, H, D, offsets, bits, tok_start, group_start, extra rows, extra groups)
-        (2, 4680, 12, 128, [0, 1560, 3120, 4680], 3, 0, 0, 0, 0),    # one next-frame block: 13 chunks per frame
+        (2, 3400, 12, 128, [0, 1700, 3400], 3, 0, 0, 0, 0),          # two 1700-row blocks: 14 chunks each
         (1, 1500, 4, 64, [0, 700, 701, 1500], 3, 24, 2, 16, 1),      # smaller, at an offset of a larger cache
     ]
     for i, (B, L, H, D, off, bits, t0, g0, xr, xg) in enumerate(cases):
