@@ -281,7 +281,11 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
     Pref P0;
     P0.g = 0;
     P0.split = false;
-    int g_run = a.split_g0[split];    // search hint: block of the last prefetched tile
+    // block of the last prefetched tile and its end (the next block's first
+    // token), kept in registers: only a tile past that end reads the block
+    // table again
+    int g_run = a.split_g0[split];
+    int e_run = a.off[g_run + 1];
 
     // words of the (packed) tile at n0 whose first token is in block g and,
     // when scales are not in LDS, that block's scales for the item's channels
@@ -334,8 +338,8 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
             }
             return;
         }
-        g_run = group_of(off, g_run, n0);
-        prefetch_words(P, n0, g_run, off[g_run + 1] < min(n0 + AT_NT, L_kv));
+        while (e_run <= n0) e_run = off[++g_run + 1];
+        prefetch_words(P, n0, g_run, e_run < min(n0 + AT_NT, L_kv));
     };
 
     // Tile 0's words, the queries and the LDS-bound scales are all in flight
