@@ -192,7 +192,7 @@ def test_kv_block_with_as_many_chunks_as_resident_workgroups(V):
 
 
 @pytest.mark.parametrize("bits", [2, 4, 7, 8])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [48, 64, 128, 256])
 def test_kv_slab_blocks_at_their_limits(V, bits, D):
     """Long blocks after short ones go to the slab kernel (one work-group per
     block and 16- or 32-channel slab, no exchange; each block takes the
@@ -203,6 +203,7 @@ def test_kv_slab_blocks_at_their_limits(V, bits, D):
     larger cache, V a strided view."""
     _say(f"[kv slab D={D} b{bits}]")
     T = 16384 // D
+    # head_dim 48: 16-channel slabs only (256/512/1024 threads: 2048/4096/8192 rows)
     sizes = [3, 5, T - 1, T + 1, 1024, 1025, 2048, 2049, 4096, 4097, 8192, 1560, T + 1]
     off = [0]
     for n in sizes:
@@ -219,7 +220,7 @@ def test_kv_slab_blocks_at_their_limits(V, bits, D):
 
 
 @pytest.mark.parametrize("bits", [3, 5, 6])
-@pytest.mark.parametrize("D", [40, 64, 128])
+@pytest.mark.parametrize("D", [40, 64, 128, 256])
 def test_kv_staged_slab_blocks_at_their_limits(V, bits, D):
     """At 3, 5 and 6 bits long blocks after short ones go to the staged slab
     kernel (40-, 24-, 40-channel slabs whose words are assembled from code
