@@ -310,10 +310,12 @@ bool staged_bits(int bits) { return bits == 3 || bits == 5 || bits == 6; }
 int slab_capacity(const SlabRun &r) { return r.nt / (r.sw / 8) * r.rpt; }
 
 // The work-group shape for a block of n rows: 32-channel slabs (64 B of each
-// row) where head_dim allows, else 16; 256, 512 or 1024 threads; 4, 8 or 16
-// row steps per thread. False when no shape holds n rows.
+// row) where head_dim allows and the rows fit (4096 at 1024 threads), else 16
+// (32 B of each row: on 2304- and 4096-row blocks these measured 1.05x the
+// algorithmic HBM bytes, 32-channel slabs 1.006x); 256, 512 or 1024 threads;
+// 4, 8 or 16 row steps per thread. False when no shape holds n rows.
 bool slab_shape(int n, int D, SlabRun &r) {
-    static const int shapes32[][2] = {{32, 256}, {32, 512}, {16, 512}, {16, 1024}};
+    static const int shapes32[][2] = {{32, 256}, {32, 512}, {32, 1024}, {16, 1024}};
     static const int shapes16[][2] = {{16, 256}, {16, 512}, {16, 1024}};
     const bool by32 = D % 32 == 0;
     const int ns = by32 ? 4 : 3;
