@@ -258,13 +258,13 @@ __device__ inline void codes8(const uint4 &w, const float (&s8)[8], const float 
     for (int j = 0; j < 4; ++j) {
         const float xl = bf16lo(wv[j]), xh = bf16hi(wv[j]);
         if (FAST_ONLY) {
-            f[2 * j] = (uint32_t)code_fast(xl, s8[2 * j], y8[2 * j]);
-            f[2 * j + 1] = (uint32_t)code_fast(xh, s8[2 * j + 1], y8[2 * j + 1]);
+            f[2 * j] = code_fast_bits(xl, s8[2 * j], y8[2 * j]);
+            f[2 * j + 1] = code_fast_bits(xh, s8[2 * j + 1], y8[2 * j + 1]);
         } else {
-            f[2 * j] = (uint32_t)(fast_scale_ok(s8[2 * j]) ? code_fast(xl, s8[2 * j], y8[2 * j])
-                                                           : code_exact(xl, s8[2 * j]));
-            f[2 * j + 1] = (uint32_t)(fast_scale_ok(s8[2 * j + 1]) ? code_fast(xh, s8[2 * j + 1], y8[2 * j + 1])
-                                                                   : code_exact(xh, s8[2 * j + 1]));
+            f[2 * j] = fast_scale_ok(s8[2 * j]) ? code_fast_bits(xl, s8[2 * j], y8[2 * j])
+                                                : code_exact_bits(xl, s8[2 * j]);
+            f[2 * j + 1] = fast_scale_ok(s8[2 * j + 1]) ? code_fast_bits(xh, s8[2 * j + 1], y8[2 * j + 1])
+                                                        : code_exact_bits(xh, s8[2 * j + 1]);
         }
     }
 }
@@ -752,12 +752,15 @@ __global__ __launch_bounds__(NT) void quant_slab_kernel(const SlabArgs a) {
     // ---- all row loads in flight at once
     const uint16_t *x = a.x[t] + (int64_t)b * a.sx_b[t] + (int64_t)h * a.sx_h[t] + (int64_t)row0 * a.sx_l[t] +
                         c * SW + 8 * q;
-    const int64_t sl = a.sx_l[t];
+    // the row stride in bytes fits 32 bits (the host checks), so a row address
+    // is one 32 x 32 -> 64-bit multiply-add
+    const char *xb = reinterpret_cast<const char *>(x);
+    const uint32_t slb = (uint32_t)a.sx_l[t] * 2u;
     uint4 xv[RPT];
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-        const int r = min(r0 + k * RS, n - 1);
-        xv[k] = *reinterpret_cast<const uint4 *>(x + (int64_t)r * sl);
+        const uint32_t r = (uint32_t)min(r0 + k * RS, n - 1);
+        xv[k] = *reinterpret_cast<const uint4 *>(xb + (uint64_t)r * slb);
     }
 
     // ---- absmax: packed 16-bit maxima of |x| (bf16 patterns with the sign
@@ -809,7 +812,9 @@ __global__ __launch_bounds__(NT) void quant_slab_kernel(const SlabArgs a) {
     const bool fast = __builtin_amdgcn_readfirstlane(sh_slow) == 0;
     constexpr int CPW = 32 / BITS;
     const int ch0 = c * SW + 8 * q;                // the lane's first channel
-    uint32_t *pk = a.packed[t] + (int64_t)bh * a.W * a.L_cap + a.tok_start + row0;
+    // the lane's word plane from its first row on; row r0 + k * RS is then a
+    // constant offset
+    uint32_t *pw = a.packed[t] + ((int64_t)bh * a.W + ch0 / CPW) * a.L_cap + a.tok_start + row0 + r0;
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
         const int r = r0 + k * RS;
@@ -821,7 +826,7 @@ __global__ __launch_bounds__(NT) void quant_slab_kernel(const SlabArgs a) {
             uint32_t w = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) w = __builtin_amdgcn_alignbit(f[j], w, 4);
-            if (r < n) pk[(int64_t)(ch0 / CPW) * a.L_cap + r] = w;
+            if (r < n) pw[k * RS] = w;
         } else if constexpr (BITS == 7 || BITS == 8) {
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -831,8 +836,8 @@ __global__ __launch_bounds__(NT) void quant_slab_kernel(const SlabArgs a) {
             }
             if constexpr (BITS == 7) { w0 >>= 4; w1 >>= 4; }     // 28 bits used
             if (r < n) {
-                pk[(int64_t)(ch0 / CPW) * a.L_cap + r] = w0;
-                pk[(int64_t)(ch0 / CPW + 1) * a.L_cap + r] = w1;
+                pw[k * RS] = w0;
+                pw[a.L_cap + k * RS] = w1;
             }
         } else {
             // 2 bits: this lane's 8 fields are one half of a 16-channel word;
@@ -842,7 +847,7 @@ __global__ __launch_bounds__(NT) void quant_slab_kernel(const SlabArgs a) {
             for (int j = 0; j < 8; ++j) w = __builtin_amdgcn_alignbit(f[j], w, 2);
             const uint32_t half = w >> 16;
             const uint32_t other = __shfl_xor(half, 1);
-            if ((q & 1) == 0 && r < n) pk[(int64_t)(ch0 / CPW) * a.L_cap + r] = half | (other << 16);
+            if ((q & 1) == 0 && r < n) pw[k * RS] = half | (other << 16);
         }
     }
 }
@@ -897,14 +902,16 @@ __global__ __launch_bounds__(NT) void quant_slab_staged_kernel(const SlabArgs a)
     // ---- all row loads in flight at once (rows past n re-read row n - 1)
     const uint16_t *x = a.x[t] + (int64_t)b * a.sx_b[t] + (int64_t)h * a.sx_h[t] + (int64_t)row0 * a.sx_l[t] +
                         ch0 + 8 * q;
-    const int64_t sl = a.sx_l[t];
+    // the row stride in bytes fits 32 bits (the host checks)
+    const char *xb = reinterpret_cast<const char *>(x);
+    const uint32_t slb = (uint32_t)a.sx_l[t] * 2u;
     uint4 xv[RPT];
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
         xv[k] = make_uint4(0, 0, 0, 0);
         if (active && k < steps) {
-            const int r = min(r0 + k * rs, n - 1);
-            xv[k] = *reinterpret_cast<const uint4 *>(x + (int64_t)r * sl);
+            const uint32_t r = (uint32_t)min(r0 + k * rs, n - 1);
+            xv[k] = *reinterpret_cast<const uint4 *>(xb + (uint64_t)r * slb);
         }
     }
 

@@ -38,20 +38,26 @@ __host__ __device__ inline bool fast_scale_ok(float s) { return s == 0.0f || s >
 // r = x*y is within an ulp of x/s; the residual e = x - r*s is exact under a
 // fused multiply-add, and r + e*y rounds to the correctly rounded quotient
 // (Markstein's correction step with a correctly rounded reciprocal y).
-__host__ __device__ inline int32_t code_fast(float x, float s, float y) {
+// The _bits forms return the rounded float's bit pattern, whose low 22 bits
+// hold the code in two's complement (the magic constant has none there):
+// packing, which keeps only a code's low BITS bits, needs no more.
+__host__ __device__ inline uint32_t code_fast_bits(float x, float s, float y) {
     float r = x * y;
     float e = __builtin_fmaf(-r, s, x);
     float qf = __builtin_fmaf(e, y, r);
-    float t = qf + kRoundMagic;
-    return (int32_t)(f2u(t) - kRoundMagicBits);
+    return f2u(qf + kRoundMagic);
+}
+__host__ __device__ inline int32_t code_fast(float x, float s, float y) {
+    return (int32_t)(code_fast_bits(x, s, y) - kRoundMagicBits);
 }
 
 // The same code by IEEE division (used for scales below kFastScaleMin).
+__host__ __device__ inline uint32_t code_exact_bits(float x, float s) {
+    if (s == 0.0f) return kRoundMagicBits;
+    return f2u(x / s + kRoundMagic);
+}
 __host__ __device__ inline int32_t code_exact(float x, float s) {
-    if (s == 0.0f) return 0;
-    float qf = x / s;
-    float t = qf + kRoundMagic;
-    return (int32_t)(f2u(t) - kRoundMagicBits);
+    return (int32_t)(code_exact_bits(x, s) - kRoundMagicBits);
 }
 
 // bf16 bit pattern of the fp32 value v, round to nearest even (finite v).
