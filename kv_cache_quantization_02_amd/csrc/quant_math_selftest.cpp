@@ -6,7 +6,8 @@
 // kernels' code for x under s = fp32(a / qmax) must equal rint(fl32(x / s))
 // computed with the host's IEEE division. Negative x follow by symmetry of both
 // rounding steps. Scales below kFastScaleMin take the division path in the
-// kernels and are checked through code_exact().
+// kernels and are checked through code_exact(). The bit-pattern forms that the
+// packers use must carry the same code in their low 8 bits, for x and -x.
 #include <stdint.h>
 
 #include <atomic>
@@ -43,7 +44,11 @@ long long varq_selftest_codes_exhaustive(int bits, int n_threads, long long *che
                 const float x = bf16_to_f32(x16);
                 const int32_t got = fast ? varq::code_fast(x, s, y) : varq::code_exact(x, s);
                 const int32_t ref = (int32_t)std::nearbyint(x / s);
-                lb += (got != ref);
+                // the packers keep the low bits of the rounded float's pattern:
+                // they must be the code's two's complement low bits, for x and -x
+                const uint32_t gp = fast ? varq::code_fast_bits(x, s, y) : varq::code_exact_bits(x, s);
+                const uint32_t gn = fast ? varq::code_fast_bits(-x, s, y) : varq::code_exact_bits(-x, s);
+                lb += (got != ref) || ((gp ^ (uint32_t)ref) & 0xFFu) != 0 || ((gn ^ (uint32_t)-ref) & 0xFFu) != 0;
                 ++lt;
             }
         }
