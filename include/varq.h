@@ -24,8 +24,9 @@
  *  - `group_offsets` is a HOST array of G+1 int32 prefix offsets
  *    0 = o_0 < o_1 < ... < o_G: block g covers tokens [o_g, o_{g+1}).
  *    G <= VARQ_MAX_GROUPS per call.
- *  - Strides are in elements. The channel (head_dim) stride is 1 ("BLHc"
- *    layout of the README's qkv_format: [batch, token, head, channel]).
+ *  - Strides are in elements and non-negative (VARQ_EINVAL otherwise). The
+ *    channel (head_dim) stride is 1 ("BLHc" layout of the README's
+ *    qkv_format: [batch, token, head, channel]).
  *  - `stream` is a hipStream_t (NULL = the default stream). Every compute call
  *    only enqueues work on that stream and returns; results are ready when the
  *    stream reaches them. No call synchronizes the stream except

@@ -408,6 +408,7 @@ int qp_setup(const void *x, int64_t sx_b, int64_t sx_l, int64_t sx_h,
     if (L_in == 0 && G_in == 0) { *empty = true; return ok(); }    // nothing to write
     if (int r = check_offsets(group_offsets, G_in, L_in, "quantize_pack")) return r;
     if (!x || !packed || !scales) return fail(VARQ_EINVAL, "quantize_pack: NULL tensor pointer");
+    if (sx_b < 0 || sx_l < 0 || sx_h < 0) return fail(VARQ_EINVAL, "quantize_pack: negative stride");
     if (!aligned(x, 16) || sx_b % 8 || sx_l % 8 || sx_h % 8)
         return fail(VARQ_EALIGN, "quantize_pack: x must be 16-byte aligned with strides that are multiples of 8");
     if (!aligned(packed, 16) || L_cap % 8)
@@ -702,6 +703,7 @@ int varq_quantize_pack_grouped(const void *x, int64_t sx_b, int64_t sx_l, int64_
                                   scales, 1, 0, workspace, workspace_bytes, stream);
     }
     if (!x || !packed || !scales) return fail(VARQ_EINVAL, "quantize_pack_grouped: NULL tensor pointer");
+    if (sx_b < 0 || sx_l < 0 || sx_h < 0) return fail(VARQ_EINVAL, "quantize_pack_grouped: negative stride");
     if (!aligned(x, 16) || sx_b % 8 || sx_l % 8 || sx_h % 8)
         return fail(VARQ_EALIGN, "quantize_pack_grouped: x must be 16-byte aligned with strides that are multiples of 8");
     if (!aligned(packed, 16) || L_cap % 8)
@@ -810,6 +812,8 @@ int packed_attention_impl(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_
         return fail(VARQ_EINVAL, "packed_attention: NULL tensor pointer");
     if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f)
         return fail(VARQ_EINVAL, "packed_attention: softmax_scale must be finite and > 0");
+    if (sq_b < 0 || sq_l < 0 || sq_h < 0 || so_b < 0 || so_l < 0 || so_h < 0)
+        return fail(VARQ_EINVAL, "packed_attention: negative stride");
     if (!aligned(q, 16) || sq_b % 8 || sq_l % 8 || sq_h % 8)
         return fail(VARQ_EALIGN, "packed_attention: q must be 16-byte aligned with strides that are multiples of 8");
     if (!aligned(out, 8) || so_b % 4 || so_l % 4 || so_h % 4)
@@ -915,6 +919,8 @@ int varq_bf16_attention(const void *q, int64_t sq_b, int64_t sq_l, int64_t sq_h,
     if (!q || !k || !v || !out) return fail(VARQ_EINVAL, "bf16_attention: NULL tensor pointer");
     if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f)
         return fail(VARQ_EINVAL, "bf16_attention: softmax_scale must be finite and > 0");
+    if (sq_b < 0 || sq_l < 0 || sq_h < 0 || so_b < 0 || so_l < 0 || so_h < 0)
+        return fail(VARQ_EINVAL, "bf16_attention: negative stride");
     if (!aligned(q, 16) || sq_b % 8 || sq_l % 8 || sq_h % 8)
         return fail(VARQ_EALIGN, "bf16_attention: q must be 16-byte aligned with strides that are multiples of 8");
     if (!aligned(out, 8) || so_b % 4 || so_l % 4 || so_h % 4)

@@ -90,6 +90,8 @@ def test_quantize_pack_validation(V):
     assert _qp(V, x=0) == -1 and _qp(V, packed=0) == -1 and _qp(V, scales=0) == -1
     assert _qp(V, x=0x10008) == -3                             # misaligned x
     assert _qp(V, sx_l=16 * 64 + 4) == -3                      # stride not a multiple of 8
+    assert _qp(V, sx_l=-16 * 64) == -1 and "negative" in V.last_error()
+    assert _qp(V, sx_b=-680 * 16 * 64) == -1 and _qp(V, sx_h=-64) == -1
     assert _qp(V, packed=0x20004) == -3
     assert _qp(V, L_cap=684) == -3                             # capacity not a multiple of 8
     assert _qp(V, L_cap=672) == -4                             # rows beyond the cache
@@ -122,6 +124,7 @@ def test_quantize_pack_kv_validation(V):
     assert _qpkv(V, k=0) == -1 and _qpkv(V, v=0) == -1
     assert _qpkv(V, packed_v=0) == -1 and _qpkv(V, scales_v=0) == -1
     assert _qpkv(V, v=0x70008) == -3 and _qpkv(V, sv_l=16 * 64 + 4) == -3
+    assert _qpkv(V, sv_l=-16 * 64) == -1 and _qpkv(V, sk_h=-64) == -1
     assert _qpkv(V, k=0x10008) == -3
     assert _qpkv(V, packed_v=0x40004) == -3
     assert _qpkv(V, L_cap=672) == -4 and _qpkv(V, G_cap=2) == -4
@@ -221,6 +224,7 @@ def test_packed_attention_validation(V):
     assert _attn(V, scale=0.0) == -1 and _attn(V, scale=float("nan")) == -1
     assert _attn(V, q=0x10002) == -3 and _attn(V, sq_h=60) == -3
     assert _attn(V, out=0x60002) == -3 and _attn(V, so_l=16 * 64 + 2) == -3
+    assert _attn(V, sq_l=-16 * 64) == -1 and _attn(V, so_b=-256 * 16 * 64) == -1
     assert _attn(V, pk=0x20004) == -3 and _attn(V, L_cap=684) == -3
     assert _attn(V, L_cap=672, L_kv=680) == -4
     assert _attn(V, G_cap=2) == -4
@@ -241,6 +245,7 @@ def test_bf16_attention_validation(V):
     assert call(L_kv=65) == -4
     assert call(k=0x20008) == -3 and call(q=0x10002) == -3 and call(sq=(8, 8, 4)) == -3
     assert call(out=0x40002) == -3
+    assert call(sq=(64 * 16 * 64, -16 * 64, 64)) == -1 and call(so=(-64 * 16 * 64, 16 * 64, 64)) == -1
 
 
 def test_unpack_dequant_validation(V):
@@ -329,6 +334,7 @@ def test_quantize_pack_grouped_validation(V):
     assert _qpg(V, n_scales=16 * 680 - 1) == -4                # per-token & per-head needs B*H*L
     assert _qpg(V, mode=5, n_scales=0) == -4                   # per-tensor needs one
     assert _qpg(V, x=0x10008) == -3 and _qpg(V, sx_l=16 * 64 + 4) == -3
+    assert _qpg(V, sx_l=-16 * 64) == -1
     assert _qpg(V, packed=0x20004) == -3 and _qpg(V, L_cap=684) == -3
     assert _qpg(V, scales=0x30002) == -3
     assert _qpg(V, L_cap=672) == -4                            # rows beyond the cache
