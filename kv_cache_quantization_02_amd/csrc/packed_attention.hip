@@ -610,19 +610,6 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
         floatx16 s[2][QB];
         bf16x8 pop[2][QB][2];
         float lt[2][QB];
-        auto scores = [&](int tb) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[tb][qb][r] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4 *>(Kb + 32 * tb * KP + 16 * ks));
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    s[tb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][ks], s[tb][qb], 0, 0, 0);
-            }
-        };
         auto mask = [&](int tb) {
             if (masked) {
 #pragma unroll
@@ -708,8 +695,22 @@ __global__ __launch_bounds__(64 * NW) void packed_attention_v5(const AttnArgs a)
             }
         };
 
-        // half 0: scores
-        scores(0);
+        // half 0: scores, LDS operands read AT_RA steps ahead
+        {
+            bf16x8 kop[AT_RA + 1];
+#pragma unroll
+            for (int i = 0; i < AT_RA && i < KSTEPS; ++i) kop[i] = kread(0, i);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < KSTEPS; ++k) {
+                if (k + AT_RA < KSTEPS) kop[(k + AT_RA) % (AT_RA + 1)] = kread(0, k + AT_RA);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    s[0][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k % (AT_RA + 1)], qop[qb][k],
+                                                                       k == 0 ? floatx16{} : s[0][qb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         mask(0);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) { lt[0][qb] = 0.0f; lt[1][qb] = 0.0f; s[1][qb] = floatx16{}; }
